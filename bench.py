@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the attention hot path on one MI355X.
+
+One step runs every stage of the path once, each on its own workload:
+  * prefill  : bf16 causal attention with per-row lse, B=4, H=32, N=4096, d=128
+               (shaped like one 7B decoder layer);
+  * paged    : kv_append through a block table + attn_decode_paged, bf16, B=64,
+               H_q=32, H_kv=8, d=128, cached lengths uniform in [128, 8192];
+  * contig   : kv_append + attn_decode on a contiguous cache, bf16, B=32, H_q=64,
+               H_kv=8, d=128, cached lengths uniform in [1024, 32768].
+Inputs are seeded synthetic tensors already resident in HBM.  Each kernel call
+is bracketed by HIP events on the stream it runs on.
+
+Printed: ONE JSON line.  ``value`` is the prefill rate in TFLOP/s (algorithmic
+FLOPs: 4*d per visible query/key pair); the decode legs report KV GB/s (bytes of
+every valid cached K and V row, read once) in their own objects.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s & decode KV GB/s on 1 MI355X (fraction of peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_flashattention_attn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    rec = data.get(kernel)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def to_dev(x, dtype, torch):
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(seconds: float, prefill_case, prefill_raw, paged_case, paged_inp):
+    """The fp64 oracle as it stands, on a bounded sample of the same workloads."""
+    import oracle
+    out = {}
+    # prefill: whole (b, h) heads of the causal workload, one at a time
+    t0 = time.perf_counter()
+    flops = 0.0
+    heads = 0
+    c = prefill_case
+    while time.perf_counter() - t0 < seconds / 2 and heads < c.B * c.H_q:
+        b, h = divmod(heads, c.H_q)
+        Q = oracle.decode_bits(prefill_raw["q"][b:b + 1, h:h + 1], c.dtype)
+        K = oracle.decode_bits(prefill_raw["k"][b:b + 1, h:h + 1], c.dtype)
+        V = oracle.decode_bits(prefill_raw["v"][b:b + 1, h:h + 1], c.dtype)
+        oracle.one_shot(Q, K, V, c.sm_scale, causal=True)
+        flops += 4.0 * c.d * c.N * (c.N + 1) / 2
+        heads += 1
+    dt = time.perf_counter() - t0
+    out["prefill"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+                      "sample": f"{heads} of {c.B * c.H_q} (batch, head) pairs of the causal prefill, "
+                                f"one_shot in fp64, {dt:.1f} s"}
+    # decode: whole sequences of the paged workload (append + gather + attend)
+    t0 = time.perf_counter()
+    nbytes = 0
+    seqs = 0
+    pc = paged_case
+    pcache = oracle.PagedCache(paged_inp["k_pool"], paged_inp["v_pool"], paged_inp["block_table"])
+    copy_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds / 2 and seqs < pc.B:
+        b = seqs
+        heads = [(b, h) for h in range(pc.H_q)]
+        oracle.decode_step(pcache, paged_inp["q"], paged_inp["k_new"], paged_inp["v_new"], paged_inp["lens"],
+                           pc.sm_scale, pc.dtype, heads=heads)
+        nbytes += (int(paged_inp["lens"][b]) + pc.n_new) * pc.H_kv * pc.d * 2 * 2
+        seqs += 1
+    dt = time.perf_counter() - t0
+    out["decode"] = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                     "sample": f"{seqs} of {pc.B} sequences of the paged decode (append, gather, attend "
+                               f"all {pc.H_q} query heads) in fp64, {dt:.1f} s (+{copy_s:.1f} s pool copy)"}
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle time budget (0 = skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU only: this build has no multi-GPU path "
+            "(prefill and decode would shard by head / sequence with no exchange).")
+        return 2
+
+    import torch
+    import synth
+    import kv_cache_flashattention_attn_amd as K
+    K.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev_props = torch.cuda.get_device_properties(0)
+
+    # ---------------- inputs ----------------
+    t_gen = time.perf_counter()
+    pcase = synth.PREFILL_BF16_CAUSAL
+    praw = synth.prefill_inputs(pcase)
+    q, k, v = (to_dev(praw[n], pcase.dtype, torch) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((pcase.B, pcase.H_q, pcase.N), dtype=torch.float32, device="cuda")
+    log(f"prefill inputs ready ({time.perf_counter() - t_gen:.1f} s)")
+
+    gcase = synth.DECODE_PAGED
+    ginp = synth.decode_inputs(gcase)
+    g = {n: to_dev(ginp[n], gcase.dtype, torch) for n in ("q", "k_new", "v_new", "k_pool", "v_pool")}
+    g_table = torch.from_numpy(ginp["block_table"]).cuda()
+    g_lens = torch.from_numpy(ginp["lens"]).cuda()
+    g_seq = g_lens + gcase.n_new
+    g_ws = torch.empty(K.attn_decode_workspace_bytes(gcase.B, gcase.H_q, gcase.max_blocks * 16, gcase.d),
+                       dtype=torch.uint8, device="cuda")
+    g_out = torch.empty_like(g["q"])
+    g_bytes = synth.kv_bytes_read(ginp["lens"] + gcase.n_new, gcase.H_kv, gcase.d, gcase.dtype)
+    log(f"paged decode inputs ready ({time.perf_counter() - t_gen:.1f} s)")
+
+    ccase = synth.DECODE_CONTIG
+    cinp = synth.decode_inputs(ccase)
+    cdev = {n: to_dev(cinp[n], ccase.dtype, torch) for n in ("q", "k_new", "v_new", "k_cache", "v_cache")}
+    c_lens = torch.from_numpy(cinp["lens"]).cuda()
+    c_seq = c_lens + ccase.n_new
+    c_ws = torch.empty(K.attn_decode_workspace_bytes(ccase.B, ccase.H_q, ccase.max_len, ccase.d),
+                       dtype=torch.uint8, device="cuda")
+    c_out = torch.empty_like(cdev["q"])
+    c_bytes = synth.kv_bytes_read(cinp["lens"] + ccase.n_new, ccase.H_kv, ccase.d, ccase.dtype)
+    c_lens_np = cinp["lens"]
+    del cinp
+    log(f"contiguous decode inputs ready ({time.perf_counter() - t_gen:.1f} s)")
+    torch.cuda.synchronize()
+
+    legs = ["prefill", "paged_append", "paged_decode", "contig_append", "contig_decode"]
+
+    def step(ev=None):
+        def rec(i):
+            if ev is not None:
+                ev[i].record()
+        rec(0)
+        K.attn_prefill(q, k, v, causal=True, scale=pcase.sm_scale, return_lse=True, out=o, lse=lse)
+        rec(1)
+        K.kv_append(g["k_pool"], g["v_pool"], g["k_new"], g["v_new"], g_lens, g_table)
+        rec(2)
+        K.attn_decode_paged(g["q"], g["k_pool"], g["v_pool"], g_table, g_seq, scale=gcase.sm_scale,
+                            workspace=g_ws, out=g_out)
+        rec(3)
+        K.kv_append(cdev["k_cache"], cdev["v_cache"], cdev["k_new"], cdev["v_new"], c_lens)
+        rec(4)
+        K.attn_decode(cdev["q"], cdev["k_cache"], cdev["v_cache"], c_seq, scale=ccase.sm_scale,
+                      workspace=c_ws, out=c_out)
+        rec(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(events[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = {name: [] for name in legs}
+    for ev in events:
+        for i, name in enumerate(legs):
+            per[name].append(ev[i].elapsed_time(ev[i + 1]))
+    ms = {name: float(np.mean(x)) for name, x in per.items()}
+    med = {name: float(np.median(x)) for name, x in per.items()}
+    flags = K.attn_device_error_flags()
+    if flags:
+        log(f"WARNING: device error flags {flags}")
+
+    pf_flops = pcase.flops()
+    pf_tflops = pf_flops / (ms["prefill"] * 1e-3) / 1e12
+    g_gbs = g_bytes / (ms["paged_decode"] * 1e-3) / 1e9
+    c_gbs = c_bytes / (ms["contig_decode"] * 1e-3) / 1e9
+
+    def roof(bound, achieved, peak, unit, kernel, per_unit):
+        return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(kernel), "kernel": kernel,
+                "per_launch": per_unit}
+
+    result = {
+        "metric": METRIC,
+        "value": round(pf_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), SFC64)",
+        "config": {"workload": pcase.name, "B": pcase.B, "H_q": pcase.H_q, "H_kv": pcase.H_kv, "N": pcase.N,
+                   "d": pcase.d, "causal": True, "lse": True, "parallelism": "none (1 GPU)"},
+        "roofline": roof("mfma", pf_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "prefill_mfma_kernel<BF16,128,causal>",
+                         {"flops": pf_flops, "ms_mean": round(ms["prefill"], 4), "ms_median": round(med["prefill"], 4)}),
+        "decode_paged": {
+            "value": round(g_gbs, 1), "unit": "GB/s", "workload": gcase.name,
+            "kv_bytes": g_bytes, "ms_mean": round(ms["paged_decode"], 4), "ms_median": round(med["paged_decode"], 4),
+            "append_ms": round(ms["paged_append"], 4),
+            "roofline": roof("hbm", g_gbs, PEAK_HBM_GBS, "GB/s", "decode_mfma_kernel<BF16,128,paged>+merge",
+                             {"bytes": g_bytes}),
+        },
+        "decode_contig": {
+            "value": round(c_gbs, 1), "unit": "GB/s", "workload": ccase.name,
+            "kv_bytes": c_bytes, "ms_mean": round(ms["contig_decode"], 4), "ms_median": round(med["contig_decode"], 4),
+            "append_ms": round(ms["contig_append"], 4),
+            "roofline": roof("hbm", c_gbs, PEAK_HBM_GBS, "GB/s", "decode_mfma_kernel<BF16,128,contig>+merge",
+                             {"bytes": c_bytes}),
+        },
+        "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
+        "device_error_flags": flags,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle on a bounded sample ...")
+        cb = cpu_baseline(args.cpu_seconds, pcase, praw, gcase, ginp)
+        result["cpu_baseline"] = cb["prefill"]
+        result["decode_paged"]["cpu_baseline"] = cb["decode"]
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

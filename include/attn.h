@@ -1,0 +1,174 @@
+/*
+ * attn.h -- C ABI of libattn: exact softmax attention for MI355X (gfx950).
+ *
+ * The library computes softmax(scale * Q K^T) V tile by tile with an online
+ * softmax (a running maximum and normaliser per query row), so the N x N score
+ * matrix never reaches device memory.  This is the tiled method of
+ * "推理速度慢怎么办？KV Cache与Flash Attention如何加速大模型推理" (section 二) and of
+ * "KV缓存与Flash注意力" (Flash Attention — 分块技巧, 步骤2), applied to prefill and
+ * to incremental decoding against a KV cache ("推理速度慢怎么办？..." section 一;
+ * "KV Cache:推理慢的真正原因", 缓存的是什么 and 工程优化手段).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  Tensors are
+ *    dense, row-major (C order) and 16-byte aligned.  The library never
+ *    allocates, frees or keeps a pointer after a call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
+ *    Calls are asynchronous and never synchronise, except
+ *    attn_device_error_flags().
+ *  - dtype is one of ATTN_F32, ATTN_F16, ATTN_BF16; Q, K, V, caches and the
+ *    output share it (unless out_fp32 asks for an fp32 output).  lse outputs
+ *    are always fp32, natural log.
+ *  - Query head h reads KV head h / (H_q / H_kv): contiguous groups of query
+ *    heads share one K/V head (grouped-query attention, "KV Cache:推理慢的真正原因",
+ *    工程优化手段 / 2).  H_q must be a multiple of H_kv.
+ *  - Return value: ATTN_OK (0) or an error code.  On error nothing is
+ *    launched; attn_last_error() returns a message for the calling thread.
+ *  - Lengths and block ids that live in device memory cannot be checked on the
+ *    host.  Kernels never read or write outside the buffers the sizes describe:
+ *    a length beyond the capacity is clamped, an invalid block id is skipped,
+ *    and a device error flag is raised (see attn_device_error_flags()).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_dtype { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 };
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, H_q % H_kv != 0, misalignment */
+  ATTN_ERR_UNSUPPORTED = 2, /* dtype, head dimension or block size not built      */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required          */
+  ATTN_ERR_HIP = 4          /* the HIP runtime refused a launch                    */
+};
+
+/* Device error flags raised by kernels (bitwise OR), see attn_device_error_flags. */
+enum attn_device_error {
+  ATTN_DEVERR_LEN_OVERFLOW = 1, /* a length exceeded the cache capacity (clamped)   */
+  ATTN_DEVERR_BAD_BLOCK = 2,    /* a block-table entry was < 0 or >= num_blocks      */
+  ATTN_DEVERR_BAD_LEN = 4       /* a length was negative (treated as 0)              */
+};
+
+/* Head dimensions accepted (any dtype): 16, 32, 64, 128, 256 for the plain
+ * kernels; the MFMA prefill and decode kernels serve f16/bf16 at d = 64, 128. */
+
+/*
+ * attn_prefill -- attention of N queries over N keys per (batch, head).
+ *
+ *   q, o : [B, H_q, N, d]      (o is fp32 when out_fp32 != 0)
+ *   k, v : [B, H_kv, N, d]
+ *   lse  : [B, H_q, N] fp32 or NULL; lse = ln sum_j exp(scale * q_i . k_j)
+ *   causal != 0: query i sees keys j <= i only.
+ *   scale: multiplies q . k before the softmax (usually 1/sqrt(d), as in the
+ *          pages' code, "推理速度慢怎么办？..." sections 一 and 二).
+ *
+ * The result equals one-shot softmax attention up to rounding: the tiles carry
+ * a running (max, sum) pair so the final normalisation is exact
+ * ("KV缓存与Flash注意力", 数值技巧 under Flash Attention — 分块技巧).
+ * Causal runs skip key tiles wholly above the diagonal and start the longest
+ * query tiles first (the causal ordering named for FlashAttention-2 in the
+ * 版本演进 table of "KV缓存与Flash注意力").
+ * Errors: INVALID_ARG (null q/k/v/o, B/H/N < 1, H_q % H_kv, misaligned),
+ *         UNSUPPORTED (dtype, d), HIP.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H_q, int H_kv, int N, int d, int causal, float scale,
+                 int dtype, int out_fp32, void* stream);
+
+/*
+ * kv_append -- write n_new new tokens' K and V rows into a KV cache.
+ *
+ * Appending only the new token's K/V (instead of recomputing the history) is
+ * the whole point of the cache ("推理速度慢怎么办？..." section 一; the append
+ * method of the cache class in "KV Cache:推理慢的真正原因", 缓存的是什么, which
+ * writes k_new.shape[2] tokens at once).
+ *
+ *   k_new, v_new : [B, H_kv, n_new, d]
+ *   cache_lens   : device int32 [B], tokens already cached for each sequence.
+ *                  Token t of sequence b goes to position cache_lens[b] + t.
+ *                  cache_lens is read, never advanced: the caller owns lengths.
+ *   block_table == NULL: contiguous caches k_cache, v_cache [B, H_kv, max_len, d].
+ *   block_table != NULL: paged pools k_cache, v_cache [num_blocks, H_kv, block_size, d]
+ *                  and block_table: device int32 [B, max_blocks_per_seq]; token p
+ *                  of sequence b lives in block block_table[b][p / block_size] at
+ *                  row p % block_size ("KV Cache:推理慢的真正原因", 工程优化手段 / 1).
+ *                  block_size must be 16.  max_len is ignored.
+ *   contiguous: num_blocks, block_size and max_blocks_per_seq are ignored.
+ *
+ * A pure bit copy.  Positions past the capacity, or blocks outside [0, num_blocks),
+ * are skipped and raise a device error flag.
+ * Errors: INVALID_ARG, UNSUPPORTED (dtype, d, block_size != 16), HIP.
+ */
+int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+              const int32_t* cache_lens, const int32_t* block_table,
+              int B, int H_kv, int n_new, int d, int max_len,
+              int block_size, int max_blocks_per_seq, int num_blocks,
+              int dtype, void* stream);
+
+/*
+ * attn_decode -- one query per head against a contiguous KV cache.
+ *
+ *   q, o      : [B, H_q, d]   (the single new query of each head; o same dtype)
+ *   k_cache, v_cache : [B, H_kv, max_len, d]
+ *   seq_lens  : device int32 [B]; sequence b attends to keys 0 .. seq_lens[b]-1,
+ *               i.e. after the append (the decode step concatenates the new
+ *               token's K/V before attending, "推理速度慢怎么办？..." section 一).
+ *               A length of 0 yields o = 0 and lse = -inf.
+ *   lse       : [B, H_q] fp32 or NULL.
+ *   workspace : device buffer of at least
+ *               attn_decode_workspace_bytes(B, H_q, max_len, d) bytes; it holds the
+ *               split partials (the cache length is split over workgroups and the
+ *               partial results merged through their log-sum-exp).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seq_lens, void* o, float* lse,
+                int B, int H_q, int H_kv, int max_len, int d, float scale, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged -- attn_decode over a paged KV cache.
+ *
+ *   k_pool, v_pool : [num_blocks, H_kv, block_size, d], block_size == 16
+ *   block_table    : device int32 [B, max_blocks_per_seq]; token p of sequence b
+ *                    is row p % 16 of block block_table[b][p / 16]
+ *                    ("KV Cache:推理慢的真正原因", 工程优化手段 / 1. PagedAttention).
+ *   seq_lens       : device int32 [B], at most max_blocks_per_seq * 16.
+ *   workspace      : at least attn_decode_workspace_bytes(B, H_q,
+ *                    max_blocks_per_seq * block_size, d) bytes.
+ * Other arguments as attn_decode.
+ */
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      void* o, float* lse,
+                      int B, int H_q, int H_kv, int d, int block_size,
+                      int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_decode / attn_decode_paged need for a cache capacity of
+ * max_seq_len tokens per sequence.  0 on invalid sizes. */
+size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+/* Reads and clears the device error flags (enum attn_device_error) of the current
+ * device after synchronising `stream`.  Returns the flags, or -1 if HIP failed. */
+int attn_device_error_flags(void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

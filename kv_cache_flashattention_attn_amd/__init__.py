@@ -1,0 +1,215 @@
+"""Python binding of libattn: exact tiled softmax attention for MI355X (gfx950).
+
+Thin ctypes wrappers with the C ABI's names (``include/attn.h``): they check
+tensor properties, pass device pointers and the current HIP stream, and raise
+on a nonzero status.  Every step of the computation runs in the HIP kernels of
+``libattn.so``; there is no fallback.  PyTorch provides device memory and
+streams only.
+
+    attn_prefill(q, k, v, causal=False, scale=None, return_lse=False, out_fp32=False)
+    kv_append(k_cache, v_cache, k_new, v_new, cache_lens, block_table=None, num_blocks=None)
+    attn_decode(q, k_cache, v_cache, seq_lens, scale=None, return_lse=False, workspace=None)
+    attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "AttnError", "lib", "lib_path", "attn_prefill", "kv_append", "attn_decode", "attn_decode_paged",
+    "attn_decode_workspace_bytes", "attn_device_error_flags", "attn_version", "DTYPE_CODES",
+    "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libattn.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
+          4: "ATTN_ERR_HIP"}
+EXPORTED_SYMBOLS = ("attn_prefill", "kv_append", "attn_decode", "attn_decode_paged",
+                    "attn_decode_workspace_bytes", "attn_last_error", "attn_version",
+                    "attn_device_error_flags")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so (built in-tree by ``build.build()``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is missing: build it with "
+                          "`python -m kv_cache_flashattention_attn_amd.build`")
+    L = ctypes.CDLL(lib_path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    L.kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp]
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                    vp, sz, vp]
+    L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_version.restype = ctypes.c_char_p
+    L.attn_device_error_flags.argtypes = [vp]
+    for name in ("attn_prefill", "kv_append", "attn_decode", "attn_decode_paged", "attn_device_error_flags"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise AttnError(fn, rc, lib().attn_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _code(t: torch.Tensor) -> int:
+    if t.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return DTYPE_CODES[t.dtype]
+
+
+def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                 scale: Optional[float] = None, return_lse: bool = False, out_fp32: bool = False,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """softmax(scale * Q K^T) V for q [B, H_q, N, d] and k, v [B, H_kv, N, d]."""
+    B, H_q, N, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, N, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_kv, N, d] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device)
+    rc = lib().attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                            _dev(lse, "lse", torch.float32) if return_lse else 0,
+                            B, H_q, H_kv, N, d, int(bool(causal)), scale, _code(q), int(bool(out_fp32)),
+                            _stream())
+    _check("attn_prefill", rc)
+    return (out, lse) if return_lse else out
+
+
+def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+              cache_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None) -> None:
+    """Write k_new/v_new [B, H_kv, n_new, d] at positions cache_lens[b] + t.
+
+    Contiguous caches are [B, H_kv, max_len, d]; with a block table the caches are
+    pools [num_blocks, H_kv, 16, d] and block_table is int32 [B, max_blocks_per_seq].
+    """
+    B, H_kv, n_new, d = k_new.shape
+    if v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must match")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != k_new.dtype or v_cache.dtype != k_new.dtype:
+        raise ValueError("caches must match each other and the new rows' dtype")
+    if block_table is None:
+        max_len, bs, mbps, nb = k_cache.shape[2], 16, 0, 0
+    else:
+        max_len, bs, mbps, nb = 0, k_cache.shape[2], block_table.shape[1], k_cache.shape[0]
+    rc = lib().kv_append(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_new, "k_new"),
+                         _dev(v_new, "v_new"), _dev(cache_lens, "cache_lens", torch.int32),
+                         _dev(block_table, "block_table", torch.int32), B, H_kv, n_new, d, max_len, bs,
+                         mbps, nb, _code(k_new), _stream())
+    _check("kv_append", rc)
+
+
+def attn_decode_workspace_bytes(B: int, H_q: int, max_seq_len: int, d: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, H_q, max_seq_len, d))
+
+
+def _workspace(ws: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws
+
+
+def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                scale: Optional[float] = None, return_lse: bool = False,
+                workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None):
+    """One query per head, q [B, H_q, d], against a contiguous cache [B, H_kv, max_len, d]."""
+    B, H_q, d = q.shape
+    _, H_kv, max_len, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = attn_decode_workspace_bytes(B, H_q, max_len, d)
+    workspace = _workspace(workspace, nbytes, q.device)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    rc = lib().attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
+                           _dev(lse, "lse", torch.float32) if return_lse else 0,
+                           B, H_q, H_kv, max_len, d, scale, _code(q), _dev(workspace, "workspace"),
+                           workspace.numel() * workspace.element_size(), _stream())
+    _check("attn_decode", rc)
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+                      seq_lens: torch.Tensor, scale: Optional[float] = None, return_lse: bool = False,
+                      workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None):
+    """attn_decode over pools [num_blocks, H_kv, 16, d] and an int32 block table [B, max_blocks]."""
+    B, H_q, d = q.shape
+    nb, H_kv, bs, _ = k_pool.shape
+    mbps = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = attn_decode_workspace_bytes(B, H_q, mbps * bs, d)
+    workspace = _workspace(workspace, nbytes, q.device)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    rc = lib().attn_decode_paged(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                 _dev(block_table, "block_table", torch.int32),
+                                 _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
+                                 _dev(lse, "lse", torch.float32) if return_lse else 0,
+                                 B, H_q, H_kv, d, bs, mbps, nb, scale, _code(q),
+                                 _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                 _stream())
+    _check("attn_decode_paged", rc)
+    return (out, lse) if return_lse else out
+
+
+def attn_device_error_flags() -> int:
+    """Synchronise the current stream, then read and clear the kernels' error flags."""
+    v = lib().attn_device_error_flags(_stream())
+    if v < 0:
+        raise AttnError("attn_device_error_flags", 4, "HIP call failed")
+    return v
+
+
+def attn_version() -> str:
+    return lib().attn_version().decode()

@@ -1,0 +1,353 @@
+// libattn host side: argument validation, kernel selection and launches.
+//
+// The whole library is one translation unit so that every kernel shares the
+// device error flag (common.h) without relocatable device code.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <type_traits>
+
+#include "attn.h"
+#include "common.h"
+#include "decode_mfma.h"
+#include "decode_plain.h"
+#include "kv_append.h"
+#include "prefill_mfma.h"
+#include "prefill_plain.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_F16 || dtype == ATTN_BF16; }
+
+bool plain_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+bool mfma_path(int dtype, int d, float scale) {
+  return (dtype == ATTN_F16 || dtype == ATTN_BF16) && (d == 64 || d == 128) && scale > 0.f;
+}
+
+int launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int kWorkspaceChunk = attn::kPlainChunk;  // smallest split any decode kernel uses
+static_assert(attn::kMfmaChunk % kWorkspaceChunk == 0, "chunk sizes");
+
+int splits_for(int capacity) { return (capacity + kWorkspaceChunk - 1) / kWorkspaceChunk; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t workspace_bytes(int B, int H_q, int capacity, int d) {
+  const size_t S = (size_t)splits_for(capacity);
+  return align_up((size_t)B * H_q * S * d * sizeof(float), 256) + (size_t)B * H_q * S * sizeof(float);
+}
+
+// ---------------------------------------------------------------------------
+// prefill dispatch
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+int launch_prefill_plain(const attn::PrefillArgs& a, bool causal, hipStream_t st) {
+  constexpr int ROWS = 256 / (D / 16);
+  dim3 grid((a.N + ROWS - 1) / ROWS, a.H_q, a.B);
+  if (causal)
+    hipLaunchKernelGGL((attn::prefill_plain_kernel<T, D, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn::prefill_plain_kernel<T, D, false>), grid, dim3(256), 0, st, a);
+  return launch_status("attn_prefill");
+}
+
+template <typename T>
+int prefill_plain_d(const attn::PrefillArgs& a, int d, bool causal, hipStream_t st) {
+  switch (d) {
+    case 16: return launch_prefill_plain<T, 16>(a, causal, st);
+    case 32: return launch_prefill_plain<T, 32>(a, causal, st);
+    case 64: return launch_prefill_plain<T, 64>(a, causal, st);
+    case 128: return launch_prefill_plain<T, 128>(a, causal, st);
+    case 256: return launch_prefill_plain<T, 256>(a, causal, st);
+  }
+  return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not supported", d);
+}
+
+template <typename T, int D>
+int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st) {
+  const long long n_qt = (a.N + 127) / 128;
+  const long long blocks = n_qt * a.B * a.H_q;
+  if (blocks > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: problem too large");
+  dim3 grid((unsigned)blocks);
+  if (causal)
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, false>), grid, dim3(256), 0, st, a);
+  return launch_status("attn_prefill");
+}
+
+template <typename T>
+int prefill_mfma_d(const attn::PrefillArgs& a, int d, bool causal, hipStream_t st) {
+  return d == 64 ? launch_prefill_mfma<T, 64>(a, causal, st) : launch_prefill_mfma<T, 128>(a, causal, st);
+}
+
+// ---------------------------------------------------------------------------
+// decode dispatch
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool PAGED>
+int launch_decode_plain(const attn::DecodeArgs& a, hipStream_t st) {
+  dim3 grid((a.capacity + attn::kPlainChunk - 1) / attn::kPlainChunk, a.H_q, a.B);
+  hipLaunchKernelGGL((attn::decode_plain_kernel<T, D, PAGED>), grid, dim3(256), 0, st, a);
+  return launch_status("attn_decode");
+}
+
+template <typename T, int D, bool PAGED>
+int launch_decode_mfma(const attn::DecodeArgs& a, hipStream_t st) {
+  const int G = a.H_q / a.H_kv;
+  const int n_hg = (G + 15) / 16;
+  dim3 grid((a.capacity + attn::kMfmaChunk - 1) / attn::kMfmaChunk, a.H_kv * n_hg, a.B);
+  hipLaunchKernelGGL((attn::decode_mfma_kernel<T, D, PAGED>), grid, dim3(256), 0, st, a, n_hg);
+  return launch_status("attn_decode");
+}
+
+template <typename T, int D>
+int launch_merge(const attn::DecodeArgs& a, void* o, float* lse, int chunk, hipStream_t st) {
+  attn::MergeArgs m{a.part_o, a.part_lse, a.seq_lens, o, lse, a.H_q, a.capacity, a.s_max, chunk};
+  hipLaunchKernelGGL((attn::decode_merge_kernel<T, D>), dim3(a.H_q, a.B), dim3(64), 0, st, m);
+  return launch_status("attn_decode merge");
+}
+
+template <typename T, int D, bool PAGED>
+int decode_typed(const attn::DecodeArgs& a, void* o, float* lse, bool mfma, hipStream_t st) {
+  int rc;
+  int chunk;
+  if constexpr ((D == 64 || D == 128) && !std::is_same<T, attn::F32>::value) {
+    if (mfma) {
+      rc = launch_decode_mfma<T, D, PAGED>(a, st);
+      chunk = attn::kMfmaChunk;
+    } else {
+      rc = launch_decode_plain<T, D, PAGED>(a, st);
+      chunk = attn::kPlainChunk;
+    }
+  } else {
+    rc = launch_decode_plain<T, D, PAGED>(a, st);
+    chunk = attn::kPlainChunk;
+  }
+  if (rc != ATTN_OK) return rc;
+  return launch_merge<T, D>(a, o, lse, chunk, st);
+}
+
+template <typename T, bool PAGED>
+int decode_d(const attn::DecodeArgs& a, void* o, float* lse, int d, bool mfma, hipStream_t st) {
+  switch (d) {
+    case 16: return decode_typed<T, 16, PAGED>(a, o, lse, mfma, st);
+    case 32: return decode_typed<T, 32, PAGED>(a, o, lse, mfma, st);
+    case 64: return decode_typed<T, 64, PAGED>(a, o, lse, mfma, st);
+    case 128: return decode_typed<T, 128, PAGED>(a, o, lse, mfma, st);
+    case 256: return decode_typed<T, 256, PAGED>(a, o, lse, mfma, st);
+  }
+  return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim %d not supported", d);
+}
+
+template <bool PAGED>
+int decode_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, int dtype, float scale,
+                    hipStream_t st) {
+  const bool mfma = mfma_path(dtype, d, scale);
+  switch (dtype) {
+    case ATTN_F32: return decode_d<attn::F32, PAGED>(a, o, lse, d, false, st);
+    case ATTN_F16: return decode_d<attn::F16, PAGED>(a, o, lse, d, mfma, st);
+    case ATTN_BF16: return decode_d<attn::BF16, PAGED>(a, o, lse, d, mfma, st);
+  }
+  return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: dtype %d not supported", dtype);
+}
+
+int check_decode_common(const char* fn, const void* q, const void* k, const void* v, const int32_t* lens,
+                        const void* o, int B, int H_q, int H_kv, int d, int dtype, float scale) {
+  if (!q || !k || !v || !lens || !o) return fail(ATTN_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (B < 1 || H_q < 1 || H_kv < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: B, H_q, H_kv must be >= 1", fn);
+  if (H_q % H_kv != 0) return fail(ATTN_ERR_INVALID_ARG, "%s: H_q (%d) is not a multiple of H_kv (%d)", fn, H_q, H_kv);
+  if (H_kv > 65535 || B > 65535 || H_q > 65535) return fail(ATTN_ERR_INVALID_ARG, "%s: B or heads too large", fn);
+  if (!valid_dtype(dtype)) return fail(ATTN_ERR_UNSUPPORTED, "%s: dtype %d not supported", fn, dtype);
+  if (!plain_head_dim(d)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d not supported", fn, d);
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H_q, int H_kv,
+                 int N, int d, int causal, float scale, int dtype, int out_fp32, void* stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: null tensor pointer");
+  if (B < 1 || H_q < 1 || H_kv < 1 || N < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: B, H_q, H_kv, N must be >= 1");
+  if (H_q % H_kv != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: H_q (%d) is not a multiple of H_kv (%d)", H_q, H_kv);
+  if (B > 65535 || H_q > 65535) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: B or H_q too large");
+  if (!valid_dtype(dtype)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: dtype %d not supported", dtype);
+  if (!plain_head_dim(d)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not supported", d);
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: scale must be finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: tensors must be 16-byte aligned");
+  if ((long long)N * d > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: N*d too large");
+
+  attn::PrefillArgs a{q, k, v, o, lse, B, H_q, H_kv, N, scale * attn::kLog2e, out_fp32 != 0};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool c = causal != 0;
+  if (mfma_path(dtype, d, scale)) {
+    return dtype == ATTN_BF16 ? prefill_mfma_d<attn::BF16>(a, d, c, st) : prefill_mfma_d<attn::F16>(a, d, c, st);
+  }
+  switch (dtype) {
+    case ATTN_F32: return prefill_plain_d<attn::F32>(a, d, c, st);
+    case ATTN_F16: return prefill_plain_d<attn::F16>(a, d, c, st);
+    default: return prefill_plain_d<attn::BF16>(a, d, c, st);
+  }
+}
+
+int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* cache_lens,
+              const int32_t* block_table, int B, int H_kv, int n_new, int d, int max_len, int block_size,
+              int max_blocks_per_seq, int num_blocks, int dtype, void* stream) {
+  if (!k_cache || !v_cache || !k_new || !v_new || !cache_lens)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_append: null pointer");
+  if (B < 1 || H_kv < 1 || n_new < 1) return fail(ATTN_ERR_INVALID_ARG, "kv_append: B, H_kv, n_new must be >= 1");
+  if (!valid_dtype(dtype)) return fail(ATTN_ERR_UNSUPPORTED, "kv_append: dtype %d not supported", dtype);
+  if (!plain_head_dim(d)) return fail(ATTN_ERR_UNSUPPORTED, "kv_append: head dim %d not supported", d);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(ATTN_ERR_INVALID_ARG, "kv_append: tensors must be 16-byte aligned");
+  if (block_table) {
+    if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "kv_append: block_size must be 16 (got %d)", block_size);
+    if (max_blocks_per_seq < 1 || num_blocks < 1)
+      return fail(ATTN_ERR_INVALID_ARG, "kv_append: max_blocks_per_seq and num_blocks must be >= 1");
+  } else if (max_len < 1) {
+    return fail(ATTN_ERR_INVALID_ARG, "kv_append: max_len must be >= 1");
+  }
+  attn::AppendArgs a;
+  a.k_cache = static_cast<uint4*>(k_cache);
+  a.v_cache = static_cast<uint4*>(v_cache);
+  a.k_new = static_cast<const uint4*>(k_new);
+  a.v_new = static_cast<const uint4*>(v_new);
+  a.cache_lens = cache_lens;
+  a.block_table = block_table;
+  a.B = B;
+  a.H_kv = H_kv;
+  a.n_new = n_new;
+  a.chunks_per_row = d * elem_bytes(dtype) / 16;
+  a.max_len = max_len;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  const long long total = (long long)B * H_kv * n_new * a.chunks_per_row;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "kv_append: too many rows");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (block_table)
+    hipLaunchKernelGGL((attn::kv_append_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn::kv_append_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return launch_status("kv_append");
+}
+
+size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d) {
+  if (B < 1 || H_q < 1 || max_seq_len < 1 || d < 1) return 0;
+  return workspace_bytes(B, H_q, max_seq_len, d);
+}
+
+static int decode_common(const char* fn, bool paged, const void* q, const void* k, const void* v,
+                         const int32_t* table, const int32_t* seq_lens, void* o, float* lse, int B, int H_q,
+                         int H_kv, int capacity, int mbps, int num_blocks, int d, float scale, int dtype,
+                         void* workspace, size_t workspace_bytes_given, void* stream) {
+  int rc = check_decode_common(fn, q, k, v, seq_lens, o, B, H_q, H_kv, d, dtype, scale);
+  if (rc != ATTN_OK) return rc;
+  if (capacity < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: cache capacity must be >= 1", fn);
+  const size_t need = workspace_bytes(B, H_q, capacity, d);
+  if (!workspace || workspace_bytes_given < need)
+    return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes_given);
+  if (!aligned16(workspace) || (lse && !aligned16(lse)))
+    return fail(ATTN_ERR_INVALID_ARG, "%s: workspace and lse must be 16-byte aligned", fn);
+  const int S = splits_for(capacity);
+  attn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.table = table;
+  a.seq_lens = seq_lens;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align_up((size_t)B * H_q * S * d * sizeof(float), 256));
+  a.B = B;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.capacity = capacity;
+  a.max_blocks_per_seq = mbps;
+  a.num_blocks = num_blocks;
+  a.s_max = S;
+  a.scale_log2 = scale * attn::kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return paged ? decode_dispatch<true>(a, o, lse, d, dtype, scale, st)
+               : decode_dispatch<false>(a, o, lse, d, dtype, scale, st);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* o,
+                float* lse, int B, int H_q, int H_kv, int max_len, int d, float scale, int dtype, void* workspace,
+                size_t workspace_bytes_given, void* stream) {
+  return decode_common("attn_decode", false, q, k_cache, v_cache, nullptr, seq_lens, o, lse, B, H_q, H_kv, max_len,
+                       0, 0, d, scale, dtype, workspace, workspace_bytes_given, stream);
+}
+
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                      const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d, int block_size,
+                      int max_blocks_per_seq, int num_blocks, float scale, int dtype, void* workspace,
+                      size_t workspace_bytes_given, void* stream) {
+  if (!block_table) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged: null block table");
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: block_size must be 16 (got %d)", block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged: max_blocks_per_seq and num_blocks must be >= 1");
+  if ((long long)max_blocks_per_seq * 16 > 0x7FFFFFFFLL)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged: max_blocks_per_seq too large");
+  return decode_common("attn_decode_paged", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q, H_kv,
+                       max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
+                       workspace_bytes_given, stream);
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+const char* attn_version(void) { return "libattn 0.1.0 (gfx950)"; }
+
+int attn_device_error_flags(void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return -1;
+  unsigned int v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(attn::g_device_errors), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess)
+    return -1;
+  const unsigned int zero = 0;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(attn::g_device_errors), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) !=
+      hipSuccess)
+    return -1;
+  return (int)v;
+}
+
+}  // extern "C"

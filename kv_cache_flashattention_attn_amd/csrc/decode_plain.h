@@ -1,0 +1,170 @@
+// Plain split decode on the vector ALUs (any dtype, d <= 256), and the split merge.
+//
+// A decode step attends one new query per head to every cached key
+// ("推理速度慢怎么办？KV Cache与Flash Attention如何加速大模型推理", section 一).  The
+// cache length is cut into chunks of kPlainChunk tokens, one workgroup per
+// (chunk, query head, sequence).  Each workgroup returns a normalised partial
+// output and its log-sum-exp; decode_merge_kernel combines the chunks with
+// the same running-(max, sum) identity the tiles use ("KV缓存与Flash注意力",
+// 数值技巧): weights exp(lse_c - max_c lse_c).
+//
+// Workspace layout (fp32): partial outputs [B][H_q][S_max][d] followed by the
+// partial lse [B][H_q][S_max].
+#pragma once
+#include "common.h"
+
+namespace attn {
+
+constexpr int kPlainChunk = 256;
+
+struct DecodeArgs {
+  const void* q;        // [B, H_q, d]
+  const void* k;        // contiguous [B, H_kv, max_len, d] or pool [NB, H_kv, 16, d]
+  const void* v;
+  const int32_t* table; // paged only: [B, max_blocks_per_seq]
+  const int32_t* seq_lens;
+  float* part_o;        // [B, H_q, S_max, d]
+  float* part_lse;      // [B, H_q, S_max]
+  int B, H_q, H_kv;
+  int capacity;         // max_len, or max_blocks_per_seq * 16
+  int max_blocks_per_seq;
+  int num_blocks;
+  int s_max;            // splits per (b, h_q) the workspace holds
+  float scale_log2;
+};
+
+// Length of sequence b, clamped to [0, capacity]; raises a flag when clamped.
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b, bool report) {
+  int len = a.seq_lens[b];
+  if (len < 0) {
+    if (report) raise_device_error(4);
+    len = 0;
+  }
+  if (len > a.capacity) {
+    if (report) raise_device_error(1);
+    len = a.capacity;
+  }
+  return len;
+}
+
+// Row index (in units of d elements) of token t of sequence b, KV head g.
+// Returns -1 for an invalid block id (after raising the flag once per call site).
+template <bool PAGED>
+__device__ __forceinline__ int64_t token_row(const DecodeArgs& a, int b, int g, int t) {
+  if (!PAGED) return ((int64_t)b * a.H_kv + g) * a.capacity + t;
+  const int blk = a.table[(int64_t)b * a.max_blocks_per_seq + (t >> 4)];
+  if (blk < 0 || blk >= a.num_blocks) return -1;
+  return ((int64_t)blk * a.H_kv + g) * 16 + (t & 15);
+}
+
+template <typename T, int D, bool PAGED>
+__global__ void __launch_bounds__(256) decode_plain_kernel(DecodeArgs a) {
+  __shared__ float qs[D];
+  __shared__ float sc[kPlainChunk];
+  __shared__ int64_t rows[kPlainChunk];
+  __shared__ float red[8];
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int len = clamp_len(a, b, s == 0 && h == 0 && tid == 0);
+  const int start = s * kPlainChunk;
+  if (start >= len) return;
+  const int n = min(kPlainChunk, len - start);
+  const int g = h / (a.H_q / a.H_kv);
+
+  for (int c = tid; c < D; c += 256) qs[c] = load_elem<T>(a.q, ((size_t)b * a.H_q + h) * D + c);
+  for (int t = tid; t < n; t += 256) {
+    const int64_t row = token_row<PAGED>(a, b, g, start + t);
+    if (row < 0) raise_device_error(2);
+    rows[t] = row;
+  }
+  __syncthreads();
+
+  // scores: one wave per token, lanes across d
+  for (int t = wave; t < n; t += 4) {
+    const int64_t row = rows[t];
+    float part = 0.f;
+    if (row >= 0)
+      for (int c = lane; c < D; c += 64) part = fmaf(qs[c], load_elem<T>(a.k, row * D + c), part);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += xor_shfl(part, off);
+    if (lane == 0) sc[t] = row >= 0 ? part * a.scale_log2 : kNegInf;
+  }
+  __syncthreads();
+
+  // maximum over the chunk
+  float mx = kNegInf;
+  for (int t = tid; t < n; t += 256) mx = fmaxf(mx, sc[t]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, xor_shfl(mx, off));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float base = mx == kNegInf ? 0.f : mx;
+  __syncthreads();
+
+  // weights and their sum
+  float sum = 0.f;
+  for (int t = tid; t < n; t += 256) {
+    const float p = fast_exp2(sc[t] - base);
+    sc[t] = p;
+    sum += p;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += xor_shfl(sum, off);
+  if (lane == 0) red[4 + wave] = sum;
+  __syncthreads();
+  sum = red[4] + red[5] + red[6] + red[7];
+
+  // weighted sum of value rows: one lane per output component
+  const size_t pidx = ((size_t)b * a.H_q + h) * a.s_max + s;
+  for (int c = tid; c < D; c += 256) {
+    float o = 0.f;
+    for (int t = 0; t < n; ++t) {
+      const int64_t row = rows[t];
+      if (row >= 0) o = fmaf(sc[t], load_elem<T>(a.v, row * D + c), o);
+    }
+    a.part_o[pidx * D + c] = sum > 0.f ? o / sum : 0.f;
+  }
+  if (tid == 0) a.part_lse[pidx] = sum > 0.f ? (mx + __log2f(sum)) * kLn2 : kNegInf;
+}
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* seq_lens;
+  void* o;          // [B, H_q, d]
+  float* lse;       // [B, H_q] or nullptr
+  int H_q;
+  int capacity;
+  int s_max;
+  int chunk;        // tokens per split
+};
+
+// Combine the split partials of one (sequence, query head).
+template <typename T, int D>
+__global__ void __launch_bounds__(256) decode_merge_kernel(MergeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : (len > a.capacity ? a.capacity : len);
+  const int ns = (len + a.chunk - 1) / a.chunk;
+  const size_t base = ((size_t)b * a.H_q + h) * a.s_max;
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[base + s]);
+  const float Mb = M == kNegInf ? 0.f : M;
+  float wsum = 0.f;
+  for (int s = 0; s < ns; ++s) wsum += fast_exp2((a.part_lse[base + s] - Mb) * kLog2e);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float w = fast_exp2((a.part_lse[base + s] - Mb) * kLog2e);
+      acc = fmaf(w, a.part_o[(base + s) * D + c], acc);
+    }
+    store_elem<T>(a.o, ((size_t)b * a.H_q + h) * D + c, acc * inv);
+  }
+  if (a.lse != nullptr && threadIdx.x == 0)
+    a.lse[(size_t)b * a.H_q + h] = wsum > 0.f ? Mb + __logf(wsum) : kNegInf;
+}
+
+}  // namespace attn

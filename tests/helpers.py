@@ -1,0 +1,60 @@
+"""Shared test helpers: moving storage bits to and from the device, tolerances."""
+import numpy as np
+
+try:
+    import torch
+except ImportError:  # pragma: no cover
+    torch = None
+
+TORCH_DTYPE = None
+if torch is not None:
+    TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+# Tolerances against the fp64 oracle on the same rounded inputs.
+MAX_ABS = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}
+MEAN_ABS = {"f32": 1e-5, "f16": 1e-3, "bf16": 1e-3}
+LSE_ABS = {"f32": 1e-5, "f16": 1e-3, "bf16": 1e-3}
+
+
+def to_dev(x: np.ndarray, dtype: str, device="cuda"):
+    """Storage bits (synth) -> device tensor of the matching torch dtype (bit copy)."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device)
+    return t.view(TORCH_DTYPE[dtype])
+
+
+def to_dev_i32(x: np.ndarray, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(device)
+
+
+def bits_of(t) -> np.ndarray:
+    """Device tensor -> storage bits as numpy (uint16 for 16-bit types, float32 for f32)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def values_of(t) -> np.ndarray:
+    """Device tensor -> exact fp64 values."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "O", fp32_out: bool = False):
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    lim_max = MAX_ABS[dtype]
+    lim_mean = MEAN_ABS[dtype]
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    assert mx <= lim_max, f"{what}: max-abs {mx:.3e} > {lim_max:.0e} (mean {mean:.3e})"
+    assert mean <= lim_mean, f"{what}: mean-abs {mean:.3e} > {lim_mean:.0e}"
+    return mx, mean
+
+
+def assert_lse_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "lse"):
+    finite = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), finite), f"{what}: -inf pattern differs"
+    if finite.any():
+        mx = float(np.abs(got[finite] - ref[finite]).max())
+        assert mx <= LSE_ABS[dtype], f"{what}: max-abs {mx:.3e} > {LSE_ABS[dtype]:.0e}"

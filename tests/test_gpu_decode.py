@@ -1,0 +1,173 @@
+"""GPU parity of kv_append (bit-exact) and attn_decode / attn_decode_paged (oracle tolerance)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_close, assert_lse_close, bits_of, to_dev, to_dev_i32, values_of
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_flashattention_attn_amd as k
+    k.lib()
+    assert k.attn_device_error_flags() == 0
+    return k
+
+
+def run_step(K, case, lens=None, heads=None):
+    """One append + attend step on the GPU and in the oracle; returns GPU (O, lse)."""
+    print(f"[decode] {case}", flush=True)
+    inp = synth.decode_inputs(case, lens=lens)
+    dt = case.dtype
+    lens_d = to_dev_i32(inp["lens"])
+    seq_d = to_dev_i32(inp["lens"] + case.n_new)
+    q, kn, vn = to_dev(inp["q"], dt), to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt)
+    if case.paged:
+        kc, vc = to_dev(inp["k_pool"], dt), to_dev(inp["v_pool"], dt)
+        table = to_dev_i32(inp["block_table"])
+        K.kv_append(kc, vc, kn, vn, lens_d, table)
+        o, lse = K.attn_decode_paged(q, kc, vc, table, seq_d, scale=case.sm_scale, return_lse=True)
+        ocache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
+    else:
+        kc, vc = to_dev(inp["k_cache"], dt), to_dev(inp["v_cache"], dt)
+        K.kv_append(kc, vc, kn, vn, lens_d)
+        o, lse = K.attn_decode(q, kc, vc, seq_d, scale=case.sm_scale, return_lse=True)
+        ocache = oracle.ContigCache(inp["k_cache"], inp["v_cache"])
+    torch.cuda.synchronize()
+    assert K.attn_device_error_flags() == 0
+    Oref, Lref = oracle.decode_step(ocache, inp["q"], inp["k_new"], inp["v_new"], inp["lens"],
+                                    case.sm_scale, dt, heads=heads)
+    # the append image, byte for byte (whole buffers, untouched sentinels included)
+    assert bits_of(kc).tobytes() == ocache.k.tobytes(), "K cache image differs"
+    assert bits_of(vc).tobytes() == ocache.v.tobytes(), "V cache image differs"
+    got_o, got_l = values_of(o), lse.cpu().numpy().astype(np.float64)
+    if heads is not None:
+        idx = tuple(np.array(heads).T)
+        got_o, Oref, got_l, Lref = got_o[idx], Oref[idx], got_l[idx], Lref[idx]
+    assert_close(got_o, Oref, dt)
+    assert_lse_close(got_l, Lref, dt)
+    return o, lse
+
+
+def case(paged, B, H_q, H_kv, d, dtype, lo, hi, seed, n_new=1):
+    return synth.DecodeCase("sweep", B, H_q, H_kv, d, dtype, lo, hi, paged, seed, n_new=n_new)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_chunk_boundaries(K, paged, dtype, d):
+    """Cache lengths around block (16), step (32) and chunk (256/512) boundaries."""
+    lens = np.array([0, 14, 15, 16, 30, 31, 255, 511, 512, 1023, 1500], dtype=np.int32)
+    run_step(K, case(paged, len(lens), 8, 2, d, dtype, 0, 1600, 10 + d), lens=lens)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16, 32])
+def test_decode_gqa_groups(K, paged, G):
+    run_step(K, case(paged, 3, 2 * G, 2, 128, "bf16", 1, 700, 20 + G))
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [16, 32, 256])
+def test_decode_plain_path(K, paged, dtype, d):
+    run_step(K, case(paged, 3, 4, 2, d, dtype, 1, 600, 30 + d))
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("n_new", [3, 17])
+def test_multi_token_append(K, paged, n_new):
+    run_step(K, case(paged, 4, 8, 4, 128, "bf16", 0, 90, 40 + n_new, n_new=n_new))
+
+
+def test_paged_identity_table_matches_contiguous(K):
+    """Identity block table: the paged pool is a reshaped contiguous cache."""
+    B, H_kv, H_q, d, nb = 2, 2, 8, 128, 6
+    r = np.random.Generator(np.random.SFC64(50))
+    pool_k = synth.to_storage(r.standard_normal((B * nb, H_kv, 16, d), dtype=np.float32), "bf16")
+    pool_v = synth.to_storage(r.standard_normal((B * nb, H_kv, 16, d), dtype=np.float32), "bf16")
+    qn = synth.to_storage(r.standard_normal((B, H_q, d), dtype=np.float32), "bf16")
+    table = np.arange(B * nb, dtype=np.int32).reshape(B, nb)
+    contig_k = pool_k.reshape(B, nb, H_kv, 16, d).transpose(0, 2, 1, 3, 4).reshape(B, H_kv, nb * 16, d)
+    contig_v = pool_v.reshape(B, nb, H_kv, 16, d).transpose(0, 2, 1, 3, 4).reshape(B, H_kv, nb * 16, d)
+    lens = np.array([nb * 16, 37], dtype=np.int32)
+    q = to_dev(qn, "bf16")
+    op = K.attn_decode_paged(q, to_dev(pool_k, "bf16"), to_dev(pool_v, "bf16"), to_dev_i32(table), to_dev_i32(lens))
+    oc = K.attn_decode(q, to_dev(contig_k, "bf16"), to_dev(contig_v, "bf16"), to_dev_i32(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(op.view(torch.int16), oc.view(torch.int16))
+
+
+def test_decode_zero_length_gives_zero(K):
+    lens = np.array([0, 5], dtype=np.int32)
+    c = case(False, 2, 4, 2, 128, "bf16", 0, 10, 60)
+    inp = synth.decode_inputs(c, lens=lens)
+    q = to_dev(inp["q"], "bf16")
+    o, lse = K.attn_decode(q, to_dev(inp["k_cache"], "bf16"), to_dev(inp["v_cache"], "bf16"),
+                           to_dev_i32(np.array([0, 5], np.int32)), return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(torch.isfinite(lse[1]))
+
+
+def test_bad_lengths_and_blocks_raise_device_flags(K):
+    """Out-of-range lengths and block ids are clamped/skipped and reported, never faulted on."""
+    c = case(True, 2, 4, 2, 128, "bf16", 20, 40, 70)
+    inp = synth.decode_inputs(c)
+    dt = "bf16"
+    kc, vc = to_dev(inp["k_pool"], dt), to_dev(inp["v_pool"], dt)
+    table = inp["block_table"].copy()
+    table[0, 1] = kc.shape[0] + 5          # out-of-range block id
+    table_d = to_dev_i32(table)
+    K.kv_append(kc, vc, to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt),
+                to_dev_i32(np.array([20, 1000], np.int32)), table_d)  # seq 0 writes into the bad block
+    assert K.attn_device_error_flags() & 3 != 0
+    seq = to_dev_i32(np.array([40, 10 ** 6], np.int32))   # seq 1 beyond the table's capacity
+    K.attn_decode_paged(to_dev(inp["q"], dt), kc, vc, table_d, seq)
+    flags = K.attn_device_error_flags()
+    assert flags & 1 and flags & 2
+    # contiguous: length beyond max_len
+    cc = case(False, 2, 4, 2, 128, "bf16", 5, 9, 71)
+    ci = synth.decode_inputs(cc)
+    K.attn_decode(to_dev(ci["q"], dt), to_dev(ci["k_cache"], dt), to_dev(ci["v_cache"], dt),
+                  to_dev_i32(np.array([cc.max_len + 100, -3], np.int32)))
+    flags = K.attn_device_error_flags()
+    assert flags & 1 and flags & 4
+    assert K.attn_device_error_flags() == 0   # cleared by the read
+
+
+def test_decode_deterministic(K):
+    c = case(True, 4, 16, 2, 128, "bf16", 100, 3000, 80)
+    inp = synth.decode_inputs(c)
+    dt = "bf16"
+    args = (to_dev(inp["q"], dt), to_dev(inp["k_pool"], dt), to_dev(inp["v_pool"], dt),
+            to_dev_i32(inp["block_table"]), to_dev_i32(inp["lens"]))
+    o1, o2 = K.attn_decode_paged(*args), K.attn_decode_paged(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_oracle_catches_a_corrupted_block_table(K):
+    """Teeth: swapping two table entries must break agreement with the oracle."""
+    c = case(True, 2, 8, 2, 128, "bf16", 300, 400, 90)
+    inp = synth.decode_inputs(c)
+    dt = "bf16"
+    table = inp["block_table"].copy()
+    table[0, [2, 7]] = table[0, [7, 2]]
+    seq = inp["lens"]
+    o = K.attn_decode_paged(to_dev(inp["q"], dt), to_dev(inp["k_pool"], dt), to_dev(inp["v_pool"], dt),
+                            to_dev_i32(table), to_dev_i32(seq), scale=c.sm_scale)
+    torch.cuda.synchronize()
+    pc = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
+    # attend over the first `seq` tokens without an append: reuse decode_step with n_new=0 rows
+    empty = np.zeros((c.B, c.H_kv, 0, c.d), dtype=np.uint16)
+    Oref, _ = oracle.decode_step(pc, inp["q"], empty, empty, seq, c.sm_scale, dt)
+    err = np.abs(values_of(o)[0] - Oref[0]).max()
+    assert err > 1e-2
