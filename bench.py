@@ -124,6 +124,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle time budget (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB read + 1 GiB write kernel (scale for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -192,6 +194,15 @@ def main() -> int:
         K.attn_decode(cdev["q"], cdev["k_cache"], cdev["v_cache"], c_seq, scale=ccase.sm_scale,
                       workspace=c_ws, out=c_out)
         rec(5)
+
+    if args.calibrate_copy:
+        # torch's elementwise multiply: reads 2^30 bytes, writes 2^30 bytes per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

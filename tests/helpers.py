@@ -41,13 +41,35 @@ def values_of(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "O", fp32_out: bool = False):
+def half_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Half a unit in the last place of |ref| in a 16-bit storage type (0 for f32)."""
+    if dtype == "f32":
+        return np.zeros_like(ref)
+    frac_bits = {"bf16": 7, "f16": 10}[dtype]
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-30)))
+    return np.exp2(e - frac_bits - 1)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "O", storage_slack: bool = False):
+    """max-abs / mean-abs bar against the fp64 oracle.
+
+    ``storage_slack``: the output is stored in a 16-bit type, and rounding the
+    exact value to that type alone costs up to half an ulp (0.0156 for |O| in
+    [4, 8) in bf16); the bar then applies to the arithmetic and each element may
+    carry its own storage rounding on top.  The arithmetic alone is checked
+    separately through the kernels' fp32-output mode.
+    """
     err = np.abs(got - ref)
     mx, mean = float(err.max()), float(err.mean())
     lim_max = MAX_ABS[dtype]
     lim_mean = MEAN_ABS[dtype]
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    assert mx <= lim_max, f"{what}: max-abs {mx:.3e} > {lim_max:.0e} (mean {mean:.3e})"
+    if storage_slack:
+        excess = err - half_ulp(ref, dtype)
+        assert float(excess.max()) <= lim_max, \
+            f"{what}: max-abs beyond storage rounding {float(excess.max()):.3e} > {lim_max:.0e}"
+    else:
+        assert mx <= lim_max, f"{what}: max-abs {mx:.3e} > {lim_max:.0e} (mean {mean:.3e})"
     assert mean <= lim_mean, f"{what}: mean-abs {mean:.3e} > {lim_mean:.0e}"
     return mx, mean
 

@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_close, assert_lse_close, to_dev, values_of
+from helpers import assert_close, assert_lse_close, bits_of, to_dev, values_of
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -29,8 +29,19 @@ def run_case(K, seed, B, H_q, H_kv, N, d, dtype, causal, out_fp32=False, scale=N
     torch.cuda.synchronize()
     Q, Kk, V = (oracle.decode_bits(raw[n], dtype) for n in ("q", "k", "v"))
     Oref, Lref = oracle.one_shot(Q, Kk, V, scale, causal)
-    assert_close(values_of(o), Oref, dtype)
     assert_lse_close(lse.cpu().numpy().astype(np.float64), Lref, dtype)
+    if dtype == "f32" or out_fp32:
+        assert_close(values_of(o), Oref, dtype)
+        return o
+    # 16-bit output: the arithmetic (fp32-output mode) meets the bar on its own,
+    # the stored output is exactly that result rounded to nearest-even, and so
+    # differs from the oracle by at most the bar plus its own storage rounding.
+    o32 = K.attn_prefill(q, k, v, causal=causal, scale=scale, out_fp32=True)
+    torch.cuda.synchronize()
+    assert_close(values_of(o32), Oref, dtype, what="O (fp32 output)")
+    assert np.array_equal(bits_of(o), synth.to_storage(o32.cpu().numpy(), dtype)), \
+        "16-bit output is not the round-to-nearest-even of the fp32 result"
+    assert_close(values_of(o), Oref, dtype, storage_slack=True)
     return o
 
 
