@@ -100,10 +100,15 @@ int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st)
   const long long blocks = n_qt * a.B * a.H_q;
   if (blocks > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: problem too large");
   dim3 grid((unsigned)blocks);
-  if (causal)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, true>), grid, dim3(256), 0, st, a);
+  const bool lse = a.lse != nullptr;
+  if (causal && lse)
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, true, true>), grid, dim3(256), 0, st, a);
+  else if (causal)
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, true, false>), grid, dim3(256), 0, st, a);
+  else if (lse)
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, false, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, false, false>), grid, dim3(256), 0, st, a);
   return launch_status("attn_prefill");
 }
 

@@ -9,19 +9,29 @@
 // ordering listed for FlashAttention-2 in the 版本演进 table of the same page).
 //
 // Mapping onto CDNA4:
-//  * 4 waves, 32 query rows each.  A wave computes S^T = K Q^T for its rows
-//    with v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q^T kept in registers),
-//    so each lane ends up holding 32 scores of ONE query row: row max and row
-//    sum are mostly lane-local (one exchange with lane l^32 for the max; the
-//    sum is exchanged once, at the end).
+//  * 4 waves, 32 query rows each; two workgroups share a CU (<= 256 registers
+//    per lane, 64 KB of LDS each), so while one wave runs its softmax on the
+//    vector ALU the other workgroup's wave on the same SIMD keeps the matrix
+//    core busy.  The two workgroups synchronise independently.
+//  * K and V tiles go straight from global memory into LDS with
+//    global_load_lds_dwordx4 (no register staging), double-buffered: tile j+1
+//    is in flight while tile j is computed; one barrier per tile.  Rows are
+//    stored with an XOR swizzle of their 16-byte chunks so that the MFMA
+//    operand reads below hit distinct banks.
+//  * A wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (A = K rows read
+//    with ds_read_b128, B = Q^T kept in registers), so each lane holds 32
+//    scores of ONE query row: the row max and sum are lane-local apart from
+//    one exchange with lane l^32.
 //  * The S^T accumulator, rounded to 16 bits, is already laid out as the B
-//    operand of O^T = V^T P^T (same lane -> query, k-slot -> token mapping), so
-//    P never leaves registers.  V is written to LDS transposed (V^T[d][token])
-//    once per tile so the A operand is two 8-byte LDS reads.
-//  * K/V tiles are double-buffered in LDS; the next tile's global loads are in
-//    flight while the current tile is computed.  One barrier per tile.
+//    operand of O^T = V^T P^T, so P never leaves registers.  The V^T operand is
+//    read from the row-major V tile with ds_read_b64_tr_b16 (gfx950's
+//    transposing LDS read: each lane of a 16-lane group receives one column of
+//    the 4 x 16 block the group addresses).
 //  * Scores are in the base-2 domain: t = s * scale * log2(e), weights
-//    exp2(t - m) (v_exp_f32), lse = (m + log2 l) ln 2.
+//    exp2(t - m) (v_exp_f32), lse = (m + log2 l) ln 2.  The reference maximum m
+//    of a row is only raised when a tile's maximum exceeds it by more than
+//    kRescaleSlack (weights stay <= 2^8, exact in fp32 accumulation), so the
+//    O accumulator is rescaled on a few tiles only, not on every tile.
 //  * Workgroup order: consecutive workgroup ids walk the (batch, head) pairs, so
 //    all query tiles of one head land on the same XCD (ids are dealt round-robin
 //    to the 8 XCDs) and share its L2; for causal runs the longest tiles go first.
@@ -30,6 +40,10 @@
 #include "prefill_plain.h"
 
 namespace attn {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <typename T>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
@@ -44,25 +58,101 @@ __device__ __forceinline__ f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int BM = 128, BN = 64;
-  constexpr int KS = D / 16;          // 16-deep k-steps of Q K^T
-  constexpr int DB = D / 32;          // 32-wide blocks of the output's d
-  constexpr int KSTR = D + 8;         // K tile row stride (elements); +16 B staggers banks
-  constexpr int VSTR = BN + 4;        // V^T row stride (elements): 136 B, 8-byte aligned
-  constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int KROWS = 256 / CPR;    // K rows loaded per pass
-  constexpr int KPASS = BN / KROWS;
-  constexpr int VPAIRS = 256 / CPR;   // V token pairs per pass
-  constexpr int VPASS = (BN / 2) / VPAIRS;
-  static_assert(KPASS >= 1 && VPASS >= 1, "tile shape");
+// Two fp32 values -> two 16-bit values (round to nearest even) in one register.
+template <typename T>
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t cvt_pk<BF16>(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+template <>
+__device__ __forceinline__ uint32_t cvt_pk<F16>(float a, float b) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+// Sum of the two 16-bit values packed in `x`, added to `acc` (v_dot2 with 1.0).
+// The normaliser of O is accumulated from the ROUNDED weights that the P V
+// product uses, so numerator and denominator see the same weights (a row whose
+// softmax is one-hot returns that V row exactly).  The lse, when requested,
+// is taken from a separate fp32 sum of the unrounded weights.
+template <typename T>
+__device__ __forceinline__ float add_pair(uint32_t x, float acc);
+template <>
+__device__ __forceinline__ float add_pair<BF16>(uint32_t x, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair<F16>(uint32_t x, float acc) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, x), __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc,
+                                false);
+}
+
+constexpr float kRescaleSlack = 8.0f;  // log2 units: weights never exceed 2^8
+
+// s_waitcnt operand (gfx9 encoding) that waits for vmcnt == 0 only.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// One wave-wide global -> LDS copy: lane l moves 16 bytes from `src` to LDS
+// byte address lds_base + 16 l (global_load_lds_dwordx4; lds_base is
+// wave-uniform and goes through M0, which is saved and restored).  Written as
+// inline assembly so that the compiler does not treat the copy as a possible
+// writer of every later LDS read: completion is awaited explicitly (vmcnt)
+// before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Geometry of the K / V tiles in LDS for head dimension D (16-bit elements).
+template <int D>
+struct PrefillGeom {
+  static constexpr int BM = 128, BN = 64;
+  static constexpr int ROWB = D * 2;                 // bytes per row
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int RPL = 256 / ROWB;             // rows per 256-byte bank line (1 or 2)
+  static constexpr int TILE = BN * ROWB;             // bytes per K or V tile
+  static constexpr int ROWS_PER_COPY = 1024 / ROWB;  // rows one wave-wide 16 B/lane copy fills
+  static constexpr int COPIES = TILE / 1024 / 4;     // copies per wave per tile (4 waves)
+  // Stored chunk position of logical chunk c of row r (K): rows that the K
+  // operand read touches together (16 consecutive rows) use distinct positions.
+  static __device__ __forceinline__ int swz_k(int r) { return (r / RPL) % CH; }
+  // V: the transposing read touches chunk pairs {2m, 2m+1} of 4 consecutive rows.
+  static __device__ __forceinline__ int swz_v(int r) { return 2 * ((r / RPL) % (CH / 2)); }
+};
+
+template <typename T, int D, bool CAUSAL, bool LSE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+prefill_mfma_kernel(PrefillArgs a) {
+  using Gm = PrefillGeom<D>;
+  constexpr int BM = Gm::BM, BN = Gm::BN, ROWB = Gm::ROWB, CH = Gm::CH, TILE = Gm::TILE;
+  constexpr int KS = D / 16;  // 16-deep k-steps of Q K^T
+  constexpr int DB = D / 32;  // 32-wide blocks of the output's d
+  static_assert(Gm::COPIES >= 1, "tile shape");
+
+  // [buffer][K, V] tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][TILE];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lr = l & 31, hh = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int l = tid & 63, lr = l & 31, hh = l >> 5;
   const int BH = a.B * a.H_q;
   const int n_qt = (a.N + BM - 1) / BM;
   const int bid = blockIdx.x;
@@ -71,14 +161,37 @@ __global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillArgs a) {
   const int b = bh / a.H_q, h = bh % a.H_q;
   const int g = h / (a.H_q / a.H_kv);
   const int q0 = qt * BM;
-  const int qw0 = q0 + 32 * w;        // first query row of this wave
-  const int qi = qw0 + lr;            // this lane's query row
-  const float c = a.scale_log2;       // > 0 on this path
+  const int qw0 = q0 + 32 * w;  // first query row of this wave
+  const int qi = qw0 + lr;      // this lane's query row
+  const float c = a.scale_log2; // > 0 on this path
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* vp = static_cast<const uint16_t*>(a.v);
   const size_t kv_base = ((size_t)b * a.H_kv + g) * (size_t)a.N * D;
+
+  const int key_end = CAUSAL ? min(a.N, q0 + BM) : a.N;
+  const int n_kt = (key_end + BN - 1) / BN;
+  // tiles every row of the workgroup sees in full (no mask, no skip)
+  const int n_full = CAUSAL ? min((q0 + 1) / BN, a.N / BN) : a.N / BN;
+  const uint32_t smem_base = lds_addr(&smem[0][0][0]);
+
+  // global -> LDS copy of one K and one V tile: this wave fills COPIES 1 KB
+  // slices of each; lane l fills stored chunk l % CH of row r.
+  auto issue_tile = [&](int k0, int buf) {
+#pragma unroll
+    for (int i = 0; i < Gm::COPIES; ++i) {
+      const int slice = w * Gm::COPIES + i;
+      const int r = slice * Gm::ROWS_PER_COPY + l / CH;
+      const int p = l % CH;
+      const int key = min(k0 + r, a.N - 1);
+      const uint16_t* row = kp + kv_base + (size_t)key * D;
+      lds_copy16(row + 8 * (p ^ Gm::swz_k(r)), smem_base + (2 * buf + 0) * TILE + slice * 1024);
+      lds_copy16(vp + (row - kp) + 8 * (p ^ Gm::swz_v(r)), smem_base + (2 * buf + 1) * TILE + slice * 1024);
+    }
+  };
+
+  issue_tile(0, 0);
 
   // Q^T fragments (B operand): lane -> query qi, k-slots -> d = 16 ks + 8 hh + j
   u32x4 qf[KS];
@@ -94,127 +207,118 @@ __global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillArgs a) {
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m = kNegInf, lsum = 0.f;
+  float m = kNegInf, lsum = 0.f, lexact = 0.f;
 
-  const int key_end = CAUSAL ? min(a.N, q0 + BM) : a.N;
-  const int n_kt = (key_end + BN - 1) / BN;
+  // V operand (transposing read): 16-lane group G = l / 16 addresses rows
+  // key0 + (l % 16) / 4 at columns 32 db + 16 (G & 1) + 4 (l % 4).
+  const int vg = l >> 4, vrow = (l & 15) >> 2, vq = l & 3;
 
-  // register staging for one K tile and one V tile
-  u32x4 kreg[KPASS];
-  u32x4 vreg[VPASS][2];
-  const int kc = tid % CPR, kr = tid / CPR;
-
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int key = k0 + kr + KROWS * i;
-      kreg[i] = key < a.N ? *reinterpret_cast<const u32x4*>(kp + kv_base + (size_t)key * D + 8 * kc)
-                          : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < VPASS; ++i) {
-      const int key = k0 + 2 * (kr + VPAIRS * i);
-      vreg[i][0] = key < a.N ? *reinterpret_cast<const u32x4*>(vp + kv_base + (size_t)key * D + 8 * kc)
-                             : u32x4{0, 0, 0, 0};
-      vreg[i][1] = key + 1 < a.N
-                       ? *reinterpret_cast<const u32x4*>(vp + kv_base + (size_t)(key + 1) * D + 8 * kc)
-                       : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i)
-      *reinterpret_cast<u32x4*>(&Ks[buf][(kr + KROWS * i) * KSTR + 8 * kc]) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < VPASS; ++i) {
-      const int pair = kr + VPAIRS * i;
-      const u32x4 x0 = vreg[i][0], x1 = vreg[i][1];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = x0[e >> 1], hi = x1[e >> 1];
-        const uint32_t word = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-        *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * kc + e) * VSTR + 2 * pair]) = word;
-      }
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_kt; ++j) {
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](const int j, const bool masked) {
     const int buf = j & 1;
     const int k0 = j * BN;
-    if (j + 1 < n_kt) load_tile(k0 + BN);
+    const uint8_t* Kt = &smem[buf][0][0];
+    const uint8_t* Vt = &smem[buf][1][0];
 
-    const bool active = !CAUSAL || k0 <= qw0 + 31;
-    if (active) {
-      // S^T = K Q^T : two 32-token row blocks
-      f32x16 sacc[2];
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    u32x4 kf[2][2];
+    auto load_k = [&](int ks, u32x4* dst) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        sacc[rb] = f32x16{};
-        const uint16_t* krow = &Ks[buf][(32 * rb + lr) * KSTR + 8 * hh];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * ks);
-          sacc[rb] = mfma32<T>(kf, qf[ks], sacc[rb]);
-        }
+        const int r = 32 * rb + lr;
+        const int cc = (2 * ks + hh) ^ Gm::swz_k(r);
+        dst[rb] = *reinterpret_cast<const u32x4*>(Kt + r * ROWB + 16 * cc);
       }
-      // masking (diagonal tiles and the ragged end only)
-      const bool need_mask = (k0 + BN > a.N) || (CAUSAL && k0 + BN - 1 > qw0);
-      if (need_mask) {
+    };
+    load_k(0, kf[0]);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) load_k(ks + 1, kf[(ks + 1) & 1]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * rb + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool vis = key < a.N && (!CAUSAL || key <= qi);
-            if (!vis) sacc[rb][i] = kNegInf;
-          }
-      }
-      // online softmax update for this lane's query row
-      float tmax = kNegInf;
+      for (int rb = 0; rb < 2; ++rb) sacc[rb] = mfma32<T>(kf[ks & 1][rb], qf[ks], sacc[rb]);
+    }
+    if (masked) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[rb][i]);
-      tmax = fmaxf(tmax, xor_shfl(tmax, 32));
-      const float m_new = fmaxf(m, tmax * c);
-      const float base = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m - base);
-      m = m_new;
-      float psum = 0.f;
-      u32x4 pf[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(sacc[kk >> 1][8 * (kk & 1) + e], c, -base));
-          psum += p[e];
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * rb + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool vis = key < a.N && (!CAUSAL || key <= qi);
+          if (!vis) sacc[rb][i] = kNegInf;
         }
-        pf[kk] = u32x4{pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
-                       pack2<T>(p[6], p[7])};
-      }
-      lsum = fmaf(alpha, lsum, psum);
+    }
+    // online softmax for this lane's query row
+    float tmax = kNegInf;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[rb][i]);
+    tmax = fmaxf(tmax, xor_shfl(tmax, 32));
+    const float mt = tmax * c;
+    const bool raise = mt > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? mt : m;
+      const float alpha = raise ? fast_exp2(m - m_new) : 1.f;
+      m = m_new;
+      lsum *= alpha;
+      if (LSE) lexact *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      // O^T += V^T P^T
+    }
+    const float base = m == kNegInf ? 0.f : m;
+    float psum = 0.f, esum = 0.f;
+    u32x4 pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(fmaf(sacc[kk >> 1][8 * (kk & 1) + e], c, -base));
+        if (LSE) esum += p[e];
+      }
+      pf[kk] = u32x4{cvt_pk<T>(p[0], p[1]), cvt_pk<T>(p[2], p[3]), cvt_pk<T>(p[4], p[5]),
+                     cvt_pk<T>(p[6], p[7])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) psum = add_pair<T>(pf[kk][e], psum);
+    }
+    lsum += psum;
+    if (LSE) lexact += esum;
+    // O^T += V^T P^T ; k-step kk = 2 rb + jj covers keys 32 rb + 16 jj + {0..3, 8..11} + 4 hh
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* vrow = &Vt[buf][(32 * db + lr) * VSTR + 4 * hh];
+        i16x4 half[2];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * kk);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * kk + 8);
-          oacc[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kk], oacc[db]);
+        for (int u = 0; u < 2; ++u) {
+          const int row = 16 * kk + 8 * u + 4 * (vg >> 1) + vrow;
+          const int col = 32 * db + 16 * (vg & 1) + 4 * vq;
+          const int cc = (col >> 3) ^ Gm::swz_v(row);
+          half[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(Vt + row * ROWB + 16 * cc + 2 * (col & 7)));
         }
+        const u32x2 lo = __builtin_bit_cast(u32x2, half[0]), hi = __builtin_bit_cast(u32x2, half[1]);
+        oacc[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kk], oacc[db]);
       }
     }
-    if (j + 1 < n_kt) store_tile(buf ^ 1);
+  };
+
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // own copies of tile 0 done
+  __syncthreads();
+
+  for (int j = 0; j < n_full; ++j) {
+    if (j + 1 < n_kt) issue_tile((j + 1) * BN, (j + 1) & 1);
+    tile(j, false);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // own copies of tile j+1 done
     __syncthreads();
   }
+  for (int j = n_full; j < n_kt; ++j) {
+    if (j + 1 < n_kt) issue_tile((j + 1) * BN, (j + 1) & 1);
+    if (!CAUSAL || j * BN <= qw0 + 31) tile(j, true);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+  (void)CH;
 
   // epilogue: O = O_acc / l ; lse = (m + log2 l) ln 2
   const float l_tot = lsum + xor_shfl(lsum, 32);
@@ -232,11 +336,14 @@ __global__ void __launch_bounds__(256) prefill_mfma_kernel(PrefillArgs a) {
         *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d0) = f32x4{o0, o1, o2, o3};
       } else {
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.o) + orow + d0) =
-            u32x2{pack2<T>(o0, o1), pack2<T>(o2, o3)};
+            u32x2{cvt_pk<T>(o0, o1), cvt_pk<T>(o2, o3)};
       }
     }
-  if (a.lse != nullptr && hh == 0)
-    a.lse[((size_t)b * a.H_q + h) * a.N + qi] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : kNegInf;
+  if (LSE) {
+    const float e_tot = lexact + xor_shfl(lexact, 32);
+    if (hh == 0)
+      a.lse[((size_t)b * a.H_q + h) * a.N + qi] = e_tot > 0.f ? (m + __log2f(e_tot)) * kLn2 : kNegInf;
+  }
 }
 
 }  // namespace attn
