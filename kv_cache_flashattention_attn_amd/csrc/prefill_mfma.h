@@ -117,6 +117,30 @@ __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds_base) {
       : "memory");
 }
 
+// Same copy with a wave-uniform 64-bit base (SGPRs) and per-lane 32-bit byte
+// offsets (global_load_lds_dwordx4 v_off, s_base): no per-lane address math.
+__device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
+
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic)
+__device__ __forceinline__ float max_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -134,8 +158,10 @@ struct PrefillGeom {
   // Stored chunk position of logical chunk c of row r (K): rows that the K
   // operand read touches together (16 consecutive rows) use distinct positions.
   static __device__ __forceinline__ int swz_k(int r) { return (r / RPL) % CH; }
-  // V: the transposing read touches chunk pairs {2m, 2m+1} of 4 consecutive rows.
-  static __device__ __forceinline__ int swz_v(int r) { return 2 * ((r / RPL) % (CH / 2)); }
+  // V: one half-wave of the transposing read touches 4 consecutive rows at
+  // 4 consecutive chunks {4m .. 4m+3}; XOR with 4 (r mod 4) spreads them over
+  // all 64 banks.
+  static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) % (CH / 4)); }
 };
 
 template <typename T, int D, bool CAUSAL, bool LSE>
@@ -177,21 +203,42 @@ prefill_mfma_kernel(PrefillArgs a) {
   const uint32_t smem_base = lds_addr(&smem[0][0][0]);
 
   // global -> LDS copy of one K and one V tile: this wave fills COPIES 1 KB
-  // slices of each; lane l fills stored chunk l % CH of row r.
-  auto issue_tile = [&](int k0, int buf) {
+  // slices of each; lane l fills stored chunk l % CH of row r.  Tiles that lie
+  // wholly inside the sequence use a scalar tile base plus precomputed lane
+  // offsets; the ragged last tile clamps each row to the last key.
+  uint32_t koff[Gm::COPIES], voff[Gm::COPIES];
 #pragma unroll
-    for (int i = 0; i < Gm::COPIES; ++i) {
-      const int slice = w * Gm::COPIES + i;
-      const int r = slice * Gm::ROWS_PER_COPY + l / CH;
-      const int p = l % CH;
-      const int key = min(k0 + r, a.N - 1);
-      const uint16_t* row = kp + kv_base + (size_t)key * D;
-      lds_copy16(row + 8 * (p ^ Gm::swz_k(r)), smem_base + (2 * buf + 0) * TILE + slice * 1024);
-      lds_copy16(vp + (row - kp) + 8 * (p ^ Gm::swz_v(r)), smem_base + (2 * buf + 1) * TILE + slice * 1024);
+  for (int i = 0; i < Gm::COPIES; ++i) {
+    const int slice = w * Gm::COPIES + i;
+    const int r = slice * Gm::ROWS_PER_COPY + l / CH;
+    const int p = l % CH;
+    koff[i] = r * ROWB + 16 * (p ^ Gm::swz_k(r));
+    voff[i] = r * ROWB + 16 * (p ^ Gm::swz_v(r));
+  }
+  // one tensor's tile: src = K or V, off = its lane offsets, which = 0 (K) / 1 (V)
+  auto issue = [&](const uint16_t* src, const uint32_t* off, int which, int k0, int buf) {
+    const uint32_t dst = smem_base + (2 * buf + which) * TILE + w * Gm::COPIES * 1024;
+    const uint16_t* tile_base = src + kv_base + (size_t)k0 * D;
+    if (k0 + BN <= a.N) {
+#pragma unroll
+      for (int i = 0; i < Gm::COPIES; ++i) lds_copy16(tile_base, off[i], dst + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Gm::COPIES; ++i) {
+        const int r = (w * Gm::COPIES + i) * Gm::ROWS_PER_COPY + l / CH;
+        const ptrdiff_t shift = (ptrdiff_t)(min(k0 + r, a.N - 1) - (k0 + r)) * ROWB;  // <= 0: clamp to the last key
+        lds_copy16(reinterpret_cast<const uint8_t*>(tile_base) + off[i] + shift, dst + i * 1024);
+      }
     }
   };
-
-  issue_tile(0, 0);
+  auto issue_k = [&](int k0, int buf) { issue(kp, koff, 0, k0, buf); };
+  auto issue_v_full = [&](int k0, int buf) {  // a tile known to lie inside the sequence
+    const uint32_t dst = smem_base + (2 * buf + 1) * TILE + w * Gm::COPIES * 1024;
+    const uint16_t* tile_base = vp + kv_base + (size_t)k0 * D;
+#pragma unroll
+    for (int i = 0; i < Gm::COPIES; ++i) lds_copy16(tile_base, voff[i], dst + i * 1024);
+  };
+  auto issue_v = [&](int k0, int buf) { issue(vp, voff, 1, k0, buf); };
 
   // Q^T fragments (B operand): lane -> query qi, k-slots -> d = 16 ks + 8 hh + j
   u32x4 qf[KS];
@@ -213,30 +260,28 @@ prefill_mfma_kernel(PrefillArgs a) {
   // key0 + (l % 16) / 4 at columns 32 db + 16 (G & 1) + 4 (l % 4).
   const int vg = l >> 4, vrow = (l & 15) >> 2, vq = l & 3;
 
-  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](const int j, const bool masked) {
-    const int buf = j & 1;
-    const int k0 = j * BN;
-    const uint8_t* Kt = &smem[buf][0][0];
-    const uint8_t* Vt = &smem[buf][1][0];
-
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-    u32x4 kf[2][2];
-    auto load_k = [&](int ks, u32x4* dst) {
+  // S^T = K_j Q^T for the 64 keys of tile j (two 32-key row blocks).
+  auto qk = [&](const int j, f32x16* sacc) {
+    const uint8_t* Kt = &smem[j & 1][0][0];
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int r = 32 * rb + lr;
         const int cc = (2 * ks + hh) ^ Gm::swz_k(r);
-        dst[rb] = *reinterpret_cast<const u32x4*>(Kt + r * ROWB + 16 * cc);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(Kt + r * ROWB + 16 * cc);
+        sacc[rb] = mfma32<T>(kf, qf[ks], sacc[rb]);
       }
-    };
-    load_k(0, kf[0]);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) load_k(ks + 1, kf[(ks + 1) & 1]);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) sacc[rb] = mfma32<T>(kf[ks & 1][rb], qf[ks], sacc[rb]);
     }
+  };
+
+  // Mask (diagonal / ragged tiles), row maximum and the rare rescale of the
+  // running state.  Kept apart from softmax_pv so that the latter is one
+  // straight block the scheduler can interleave with the next tile's Q K^T.
+  auto row_max = [&](const int j, f32x16* sacc, const bool masked) {
+    const int k0 = j * BN;
     if (masked) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -247,13 +292,12 @@ prefill_mfma_kernel(PrefillArgs a) {
           if (!vis) sacc[rb][i] = kNegInf;
         }
     }
-    // online softmax for this lane's query row
     float tmax = kNegInf;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[rb][i]);
-    tmax = fmaxf(tmax, xor_shfl(tmax, 32));
+    tmax = max_pair32(tmax);
     const float mt = tmax * c;
     const bool raise = mt > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -265,6 +309,11 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
+  };
+
+  // Weights of tile j and O^T += V_j^T P^T.
+  auto softmax_pv = [&](const int j, const f32x16* sacc) {
+    const uint8_t* Vt = &smem[j & 1][1][0];
     const float base = m == kNegInf ? 0.f : m;
     float psum = 0.f, esum = 0.f;
     u32x4 pf[4];
@@ -283,7 +332,7 @@ prefill_mfma_kernel(PrefillArgs a) {
     }
     lsum += psum;
     if (LSE) lexact += esum;
-    // O^T += V^T P^T ; k-step kk = 2 rb + jj covers keys 32 rb + 16 jj + {0..3, 8..11} + 4 hh
+    // k-step kk = 2 rb + jj covers keys 32 rb + 16 jj + {0..3, 8..11} + 4 hh
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -303,25 +352,73 @@ prefill_mfma_kernel(PrefillArgs a) {
     }
   };
 
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // own copies of tile 0 done
+  // Software pipeline over key tiles.  Iteration j computes the weights and
+  // P V of tile j while the matrix core already runs Q K^T of tile j+1; the
+  // copies in flight during iteration j are K_{j+2} and V_{j+1}, so K_j and
+  // V_j buffers alternate independently.
+  auto active = [&](int j) { return !CAUSAL || j * BN <= qw0 + 31; };
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (n_kt > 1) issue_k(BN, 1);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // own copies done
   __syncthreads();
 
-  for (int j = 0; j < n_full; ++j) {
-    if (j + 1 < n_kt) issue_tile((j + 1) * BN, (j + 1) & 1);
-    tile(j, false);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // own copies of tile j+1 done
+  f32x16 s_cur[2], s_nxt[2];
+  if (active(0)) qk(0, s_cur);
+
+  int j = 0;
+  // steady state: tiles j and j+1 both unmasked and active for every wave.
+  // One straight block per tile: the 16 MFMAs of Q K_{j+1}^T are interleaved
+  // with the vector work of tile j's weights, then P V_j follows with its
+  // transposing reads two MFMAs ahead.
+  auto steady = [&](const int jj, f32x16* sc, f32x16* sn) {
+    if (jj + 2 < n_kt) issue_k((jj + 2) * BN, jj & 1);
+    issue_v_full((jj + 1) * BN, (jj + 1) & 1);
+    row_max(jj, sc, false);
+    qk(jj + 1, sn);
+    softmax_pv(jj, sc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 K reads
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA of Q K^T
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 K read
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0); // softmax vector work
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 V^T reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA of P V
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // own copies of K_{j+2}, V_{j+1} done
     __syncthreads();
+  };
+  for (; j + 2 < n_full; j += 2) {
+    steady(j, s_cur, s_nxt);
+    steady(j + 1, s_nxt, s_cur);
   }
-  for (int j = n_full; j < n_kt; ++j) {
-    if (j + 1 < n_kt) issue_tile((j + 1) * BN, (j + 1) & 1);
-    if (!CAUSAL || j * BN <= qw0 + 31) tile(j, true);
+  if (j + 1 < n_full) {
+    steady(j, s_cur, s_nxt);
+    s_cur[0] = s_nxt[0];
+    s_cur[1] = s_nxt[1];
+    ++j;
+  }
+  // diagonal / ragged tiles
+  for (; j < n_kt; ++j) {
+    const bool act = active(j);
+    if (act) row_max(j, s_cur, j >= n_full);
+    if (j + 2 < n_kt) issue_k((j + 2) * BN, j & 1);
+    if (j + 1 < n_kt) issue_v((j + 1) * BN, (j + 1) & 1);
+    if (j + 1 < n_kt && active(j + 1)) qk(j + 1, s_nxt);
+    if (act) softmax_pv(j, s_cur);
+    s_cur[0] = s_nxt[0];
+    s_cur[1] = s_nxt[1];
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
   (void)CH;
 
   // epilogue: O = O_acc / l ; lse = (m + log2 l) ln 2
-  const float l_tot = lsum + xor_shfl(lsum, 32);
+  const float l_tot = sum_pair32(lsum);
   if (qi >= a.N) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const size_t orow = (((size_t)b * a.H_q + h) * a.N + qi) * D;
@@ -340,7 +437,7 @@ prefill_mfma_kernel(PrefillArgs a) {
       }
     }
   if (LSE) {
-    const float e_tot = lexact + xor_shfl(lexact, 32);
+    const float e_tot = sum_pair32(lexact);
     if (hh == 0)
       a.lse[((size_t)b * a.H_q + h) * a.N + qi] = e_tot > 0.f ? (m + __log2f(e_tot)) * kLn2 : kNegInf;
   }
