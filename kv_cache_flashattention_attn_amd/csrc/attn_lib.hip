@@ -96,19 +96,20 @@ int prefill_plain_d(const attn::PrefillArgs& a, int d, bool causal, hipStream_t 
 
 template <typename T, int D>
 int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st) {
-  const long long n_qt = (a.N + 127) / 128;
+  constexpr int NW = attn::kPrefillWaves;
+  const long long n_qt = (a.N + 32 * NW - 1) / (32 * NW);
   const long long blocks = n_qt * a.B * a.H_q;
   if (blocks > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: problem too large");
-  dim3 grid((unsigned)blocks);
+  const dim3 grid((unsigned)blocks), block(64 * NW);
   const bool lse = a.lse != nullptr;
   if (causal && lse)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, true, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, true>), grid, block, 0, st, a);
   else if (causal)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, true, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, false>), grid, block, 0, st, a);
   else if (lse)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, false, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, false, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, false>), grid, block, 0, st, a);
   return launch_status("attn_prefill");
 }
 

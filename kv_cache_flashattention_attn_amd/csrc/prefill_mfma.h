@@ -32,9 +32,12 @@
 //    of a row is only raised when a tile's maximum exceeds it by more than
 //    kRescaleSlack (weights stay <= 2^8, exact in fp32 accumulation), so the
 //    O accumulator is rescaled on a few tiles only, not on every tile.
-//  * Workgroup order: consecutive workgroup ids walk the (batch, head) pairs, so
-//    all query tiles of one head land on the same XCD (ids are dealt round-robin
-//    to the 8 XCDs) and share its L2; for causal runs the longest tiles go first.
+//  * Workgroup order: the hardware deals workgroup ids round-robin to the 8
+//    XCDs, each with its own L2.  Ids are remapped so that XCD x runs a
+//    contiguous range of (batch, head) pairs, all query tiles of one head
+//    back to back: an XCD works on about two heads at a time and their K/V
+//    (2 MB at N = 4096, d = 128) stays in its 4 MB L2.  Within a head the
+//    longest causal tiles go first.
 #pragma once
 #include "common.h"
 #include "prefill_plain.h"
@@ -94,6 +97,9 @@ __device__ __forceinline__ float add_pair<F16>(uint32_t x, float acc) {
                                 false);
 }
 
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kPrefillWaves = 4;  // waves (of 32 query rows) per prefill workgroup
+
 constexpr float kRescaleSlack = 8.0f;  // log2 units: weights never exceed 2^8
 
 // s_waitcnt operand (gfx9 encoding) that waits for vmcnt == 0 only.
@@ -145,16 +151,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Geometry of the K / V tiles in LDS for head dimension D (16-bit elements).
-template <int D>
+// Geometry of the K / V tiles in LDS for head dimension D (16-bit elements)
+// and NW waves of 32 query rows per workgroup.
+template <int D, int NW>
 struct PrefillGeom {
-  static constexpr int BM = 128, BN = 64;
+  static constexpr int BM = 32 * NW, BN = 64;
   static constexpr int ROWB = D * 2;                 // bytes per row
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int RPL = 256 / ROWB;             // rows per 256-byte bank line (1 or 2)
   static constexpr int TILE = BN * ROWB;             // bytes per K or V tile
   static constexpr int ROWS_PER_COPY = 1024 / ROWB;  // rows one wave-wide 16 B/lane copy fills
-  static constexpr int COPIES = TILE / 1024 / 4;     // copies per wave per tile (4 waves)
+  static constexpr int COPIES = TILE / 1024 / NW;    // copies per wave per tile
+  // Copy i of wave w fills the 1 KB slice i * NW + w; consecutive copies of a
+  // wave are NW * ROWS_PER_COPY rows apart, a multiple of both swizzle periods
+  // below, so one lane offset serves all of them.
+  static_assert((NW * ROWS_PER_COPY) % 16 == 0, "copy stride vs swizzle period");
   // Stored chunk position of logical chunk c of row r (K): rows that the K
   // operand read touches together (16 consecutive rows) use distinct positions.
   static __device__ __forceinline__ int swz_k(int r) { return (r / RPL) % CH; }
@@ -164,10 +175,10 @@ struct PrefillGeom {
   static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) % (CH / 4)); }
 };
 
-template <typename T, int D, bool CAUSAL, bool LSE>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <typename T, int D, int NW, bool CAUSAL, bool LSE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 prefill_mfma_kernel(PrefillArgs a) {
-  using Gm = PrefillGeom<D>;
+  using Gm = PrefillGeom<D, NW>;
   constexpr int BM = Gm::BM, BN = Gm::BN, ROWB = Gm::ROWB, CH = Gm::CH, TILE = Gm::TILE;
   constexpr int KS = D / 16;  // 16-deep k-steps of Q K^T
   constexpr int DB = D / 32;  // 32-wide blocks of the output's d
@@ -181,9 +192,11 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int l = tid & 63, lr = l & 31, hh = l >> 5;
   const int BH = a.B * a.H_q;
   const int n_qt = (a.N + BM - 1) / BM;
+  const int total = n_qt * BH;
   const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int qt = CAUSAL ? (n_qt - 1 - bid / BH) : (bid / BH);
+  const int t = (total % kNumXcd == 0) ? (bid % kNumXcd) * (total / kNumXcd) + bid / kNumXcd : bid;
+  const int bh = t / n_qt;
+  const int qt = CAUSAL ? (n_qt - 1 - t % n_qt) : (t % n_qt);
   const int b = bh / a.H_q, h = bh % a.H_q;
   const int g = h / (a.H_q / a.H_kv);
   const int q0 = qt * BM;
@@ -202,43 +215,38 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int n_full = CAUSAL ? min((q0 + 1) / BN, a.N / BN) : a.N / BN;
   const uint32_t smem_base = lds_addr(&smem[0][0][0]);
 
-  // global -> LDS copy of one K and one V tile: this wave fills COPIES 1 KB
-  // slices of each; lane l fills stored chunk l % CH of row r.  Tiles that lie
-  // wholly inside the sequence use a scalar tile base plus precomputed lane
-  // offsets; the ragged last tile clamps each row to the last key.
-  uint32_t koff[Gm::COPIES], voff[Gm::COPIES];
-#pragma unroll
-  for (int i = 0; i < Gm::COPIES; ++i) {
-    const int slice = w * Gm::COPIES + i;
-    const int r = slice * Gm::ROWS_PER_COPY + l / CH;
-    const int p = l % CH;
-    koff[i] = r * ROWB + 16 * (p ^ Gm::swz_k(r));
-    voff[i] = r * ROWB + 16 * (p ^ Gm::swz_v(r));
-  }
-  // one tensor's tile: src = K or V, off = its lane offsets, which = 0 (K) / 1 (V)
-  auto issue = [&](const uint16_t* src, const uint32_t* off, int which, int k0, int buf) {
-    const uint32_t dst = smem_base + (2 * buf + which) * TILE + w * Gm::COPIES * 1024;
-    const uint16_t* tile_base = src + kv_base + (size_t)k0 * D;
+  // global -> LDS copy of one K and one V tile: copy i of this wave fills the
+  // 1 KB slice i * NW + w of each; lane l fills stored chunk l % CH of row r.
+  // Tiles that lie wholly inside the sequence use a scalar tile base plus one
+  // lane offset; the ragged last tile clamps each row to the last key.
+  const int r0 = w * Gm::ROWS_PER_COPY + l / CH;  // row of copy 0
+  const uint32_t koff = r0 * ROWB + 16 * ((l % CH) ^ Gm::swz_k(r0));
+  const uint32_t voff = r0 * ROWB + 16 * ((l % CH) ^ Gm::swz_v(r0));
+  constexpr int kCopyStride = NW * 1024;  // bytes between consecutive copies of a wave
+  // one tensor's tile: src = K or V, off = its lane offset, which = 0 (K) / 1 (V)
+  auto issue = [&](const uint16_t* src, const uint32_t off, int which, int k0, int buf) {
+    const uint32_t dst = smem_base + (2 * buf + which) * TILE + w * 1024;
+    const uint8_t* tile_base = reinterpret_cast<const uint8_t*>(src + kv_base + (size_t)k0 * D);
     if (k0 + BN <= a.N) {
 #pragma unroll
-      for (int i = 0; i < Gm::COPIES; ++i) lds_copy16(tile_base, off[i], dst + i * 1024);
+      for (int i = 0; i < Gm::COPIES; ++i) lds_copy16(tile_base + i * kCopyStride, off, dst + i * kCopyStride);
     } else {
 #pragma unroll
       for (int i = 0; i < Gm::COPIES; ++i) {
-        const int r = (w * Gm::COPIES + i) * Gm::ROWS_PER_COPY + l / CH;
+        const int r = r0 + i * NW * Gm::ROWS_PER_COPY;
         const ptrdiff_t shift = (ptrdiff_t)(min(k0 + r, a.N - 1) - (k0 + r)) * ROWB;  // <= 0: clamp to the last key
-        lds_copy16(reinterpret_cast<const uint8_t*>(tile_base) + off[i] + shift, dst + i * 1024);
+        lds_copy16(tile_base + i * kCopyStride + off + shift, dst + i * kCopyStride);
       }
     }
   };
   auto issue_k = [&](int k0, int buf) { issue(kp, koff, 0, k0, buf); };
-  auto issue_v_full = [&](int k0, int buf) {  // a tile known to lie inside the sequence
-    const uint32_t dst = smem_base + (2 * buf + 1) * TILE + w * Gm::COPIES * 1024;
-    const uint16_t* tile_base = vp + kv_base + (size_t)k0 * D;
-#pragma unroll
-    for (int i = 0; i < Gm::COPIES; ++i) lds_copy16(tile_base, voff[i], dst + i * 1024);
-  };
   auto issue_v = [&](int k0, int buf) { issue(vp, voff, 1, k0, buf); };
+  auto issue_v_full = [&](int k0, int buf) {  // a tile known to lie inside the sequence
+    const uint32_t dst = smem_base + (2 * buf + 1) * TILE + w * 1024;
+    const uint8_t* tile_base = reinterpret_cast<const uint8_t*>(vp + kv_base + (size_t)k0 * D);
+#pragma unroll
+    for (int i = 0; i < Gm::COPIES; ++i) lds_copy16(tile_base + i * kCopyStride, voff, dst + i * kCopyStride);
+  };
 
   // Q^T fragments (B operand): lane -> query qi, k-slots -> d = 16 ks + 8 hh + j
   u32x4 qf[KS];
@@ -368,9 +376,9 @@ prefill_mfma_kernel(PrefillArgs a) {
 
   int j = 0;
   // steady state: tiles j and j+1 both unmasked and active for every wave.
-  // One straight block per tile: the 16 MFMAs of Q K_{j+1}^T are interleaved
-  // with the vector work of tile j's weights, then P V_j follows with its
-  // transposing reads two MFMAs ahead.
+  // One straight block per tile: the 16 MFMAs of Q K_{j+1}^T (each with the
+  // next K read) and the vector work of tile j's weights are independent, so
+  // the scheduler interleaves them; P V_j follows with its transposing reads.
   auto steady = [&](const int jj, f32x16* sc, f32x16* sn) {
     if (jj + 2 < n_kt) issue_k((jj + 2) * BN, jj & 1);
     issue_v_full((jj + 1) * BN, (jj + 1) & 1);
@@ -382,7 +390,6 @@ prefill_mfma_kernel(PrefillArgs a) {
     for (int i = 0; i < 2 * KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA of Q K^T
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 K read
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0); // softmax vector work
     }
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
