@@ -141,29 +141,53 @@ struct MergeArgs {
   int chunk;        // tokens per split
 };
 
-// Combine the split partials of one (sequence, query head).
+// Combine the split partials of one (sequence, query head): one wave, lanes
+// across d.  The weights exp(lse_s - max lse) of all splits are computed once
+// (lane s holds split s) and broadcast; partial rows are read 512 B at a time
+// with several splits in flight.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) decode_merge_kernel(MergeArgs a) {
+__global__ void __launch_bounds__(64) decode_merge_kernel(MergeArgs a) {
+  constexpr int PER = (D + 63) / 64;  // output components per lane
   const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.capacity ? a.capacity : len);
   const int ns = (len + a.chunk - 1) / a.chunk;
   const size_t base = ((size_t)b * a.H_q + h) * a.s_max;
   float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[base + s]);
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.part_lse[base + s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
   const float Mb = M == kNegInf ? 0.f : M;
   float wsum = 0.f;
-  for (int s = 0; s < ns; ++s) wsum += fast_exp2((a.part_lse[base + s] - Mb) * kLog2e);
+  for (int s = lane; s < ns; s += 64) wsum += fast_exp2((a.part_lse[base + s] - Mb) * kLog2e);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wsum += xor_shfl(wsum, off);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = fast_exp2((a.part_lse[base + s] - Mb) * kLog2e);
-      acc = fmaf(w, a.part_o[(base + s) * D + c], acc);
+
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int cnt = min(64, ns - s0);
+    const float w_l = lane < cnt ? fast_exp2((a.part_lse[base + s0 + lane] - Mb) * kLog2e) : 0.f;
+    const float* row = a.part_o + (base + s0) * D;
+#pragma unroll 8
+    for (int s = 0; s < cnt; ++s) {
+      const float ws = __shfl(w_l, s, 64);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int c = lane + 64 * j;
+        if (c < D) acc[j] = fmaf(ws, row[(size_t)s * D + c], acc[j]);
+      }
     }
-    store_elem<T>(a.o, ((size_t)b * a.H_q + h) * D + c, acc * inv);
   }
-  if (a.lse != nullptr && threadIdx.x == 0)
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int c = lane + 64 * j;
+    if (c < D) store_elem<T>(a.o, ((size_t)b * a.H_q + h) * D + c, acc[j] * inv);
+  }
+  if (a.lse != nullptr && lane == 0)
     a.lse[(size_t)b * a.H_q + h] = wsum > 0.f ? Mb + __logf(wsum) : kNegInf;
 }
 
