@@ -142,9 +142,9 @@ struct MergeArgs {
 };
 
 // Combine the split partials of one (sequence, query head): one wave, lanes
-// across d.  The weights exp(lse_s - max lse) of all splits are computed once
-// (lane s holds split s) and broadcast; partial rows are read 512 B at a time
-// with several splits in flight.
+// across d.  The weights exp(lse_s - max lse) of 64 splits are computed at
+// once (lane s holds split s) and broadcast with v_readlane; the partial rows
+// of 16 splits are loaded before any is used, so they are in flight together.
 template <typename T, int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(MergeArgs a) {
   constexpr int PER = (D + 63) / 64;  // output components per lane
@@ -168,17 +168,26 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(MergeArgs a) {
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  constexpr int BATCH = 16;  // splits whose rows are in flight together
   for (int s0 = 0; s0 < ns; s0 += 64) {
     const int cnt = min(64, ns - s0);
     const float w_l = lane < cnt ? fast_exp2((a.part_lse[base + s0 + lane] - Mb) * kLog2e) : 0.f;
-    const float* row = a.part_o + (base + s0) * D;
-#pragma unroll 8
-    for (int s = 0; s < cnt; ++s) {
-      const float ws = __shfl(w_l, s, 64);
+    const float* rows = a.part_o + (base + s0) * D;
+    for (int s1 = 0; s1 < cnt; s1 += BATCH) {
+      float v[BATCH][PER];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int c = lane + 64 * j;
-        if (c < D) acc[j] = fmaf(ws, row[(size_t)s * D + c], acc[j]);
+      for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int c = lane + 64 * j;
+          v[u][j] = (s1 + u < cnt && c < D) ? rows[(size_t)(s1 + u) * D + c] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        // weight of split s0 + s1 + u (lanes at or past cnt hold 0)
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), (s1 + u) & 63));
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] = fmaf(ws, v[u][j], acc[j]);
       }
     }
   }
