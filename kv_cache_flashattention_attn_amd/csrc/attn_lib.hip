@@ -56,16 +56,39 @@ int launch_status(const char* what) {
   return ok();
 }
 
-constexpr int kWorkspaceChunk = attn::kPlainChunk;  // smallest split any decode kernel uses
-static_assert(attn::kMfmaChunk % kWorkspaceChunk == 0, "chunk sizes");
-
-int splits_for(int capacity) { return (capacity + kWorkspaceChunk - 1) / kWorkspaceChunk; }
+// Workspace: split partials [B][H_q][S][d] fp32, their lse [B][H_q][S] fp32,
+// then the piece counts [B][H_q] int32 of the streaming MFMA decode.  S covers
+// both the plain kernel's kPlainChunk-token splits and the MFMA kernel's pieces.
+int splits_for(int capacity) {
+  const int plain = (capacity + attn::kPlainChunk - 1) / attn::kPlainChunk;
+  const int pieces = attn::dec_max_pieces(capacity);
+  return plain > pieces ? plain : pieces;
+}
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-size_t workspace_bytes(int B, int H_q, int capacity, int d) {
+struct WorkspaceLayout {
+  size_t lse_off, cnt_off, bytes;
+};
+
+WorkspaceLayout workspace_layout(int B, int H_q, int capacity, int d) {
   const size_t S = (size_t)splits_for(capacity);
-  return align_up((size_t)B * H_q * S * d * sizeof(float), 256) + (size_t)B * H_q * S * sizeof(float);
+  WorkspaceLayout w;
+  w.lse_off = align_up((size_t)B * H_q * S * d * sizeof(float), 256);
+  w.cnt_off = align_up(w.lse_off + (size_t)B * H_q * S * sizeof(float), 256);
+  w.bytes = w.cnt_off + (size_t)B * H_q * sizeof(int32_t);
+  return w;
+}
+
+size_t workspace_bytes(int B, int H_q, int capacity, int d) { return workspace_layout(B, H_q, capacity, d).bytes; }
+
+// Workgroups of `kernel` (block of `threads`) that fit on the current device at once.
+int resident_grid(const void* kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  return cus * (per_cu > 0 ? per_cu : 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -129,61 +152,62 @@ int launch_decode_plain(const attn::DecodeArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D, bool PAGED>
-int launch_decode_mfma(const attn::DecodeArgs& a, hipStream_t st) {
+int launch_decode_mfma(const attn::DecodeArgs& a, int32_t* piece_cnt, hipStream_t st) {
   const int G = a.H_q / a.H_kv;
-  const int n_hg = (G + 15) / 16;
-  dim3 grid((a.capacity + attn::kMfmaChunk - 1) / attn::kMfmaChunk, a.H_kv * n_hg, a.B);
-  hipLaunchKernelGGL((attn::decode_mfma_kernel<T, D, PAGED>), grid, dim3(256), 0, st, a, n_hg);
+  const attn::DecodeStreamArgs sa{a, piece_cnt, (G + 15) / 16};
+  const void* kernel = reinterpret_cast<const void*>(&attn::decode_mfma_kernel<T, D, PAGED>);
+  static int grid = 0;  // one value per instantiation; every device here is an MI355X
+  if (grid == 0) grid = resident_grid(kernel, 64 * attn::kDecWaves);
+  if (grid <= 0) return fail(ATTN_ERR_HIP, "attn_decode: occupancy query failed");
+  hipLaunchKernelGGL((attn::decode_mfma_kernel<T, D, PAGED>), dim3(grid), dim3(64 * attn::kDecWaves), 0, st, sa,
+                     a.seq_lens, a.table);
   return launch_status("attn_decode");
 }
 
 template <typename T, int D>
-int launch_merge(const attn::DecodeArgs& a, void* o, float* lse, int chunk, hipStream_t st) {
-  attn::MergeArgs m{a.part_o, a.part_lse, a.seq_lens, o, lse, a.H_q, a.capacity, a.s_max, chunk};
+int launch_merge(const attn::DecodeArgs& a, void* o, float* lse, int chunk, const int32_t* piece_cnt,
+                 hipStream_t st) {
+  const int G = a.H_q / a.H_kv;
+  attn::MergeArgs m{a.part_o, a.part_lse, a.seq_lens, piece_cnt, o, lse, a.H_q, a.capacity, a.s_max, chunk,
+                    G, (G + 15) / 16};
   hipLaunchKernelGGL((attn::decode_merge_kernel<T, D>), dim3(a.H_q, a.B), dim3(64), 0, st, m);
   return launch_status("attn_decode merge");
 }
 
 template <typename T, int D, bool PAGED>
-int decode_typed(const attn::DecodeArgs& a, void* o, float* lse, bool mfma, hipStream_t st) {
-  int rc;
-  int chunk;
+int decode_typed(const attn::DecodeArgs& a, void* o, float* lse, bool mfma, int32_t* piece_cnt, hipStream_t st) {
   if constexpr ((D == 64 || D == 128) && !std::is_same<T, attn::F32>::value) {
     if (mfma) {
-      rc = launch_decode_mfma<T, D, PAGED>(a, st);
-      chunk = attn::kMfmaChunk;
-    } else {
-      rc = launch_decode_plain<T, D, PAGED>(a, st);
-      chunk = attn::kPlainChunk;
+      const int rc = launch_decode_mfma<T, D, PAGED>(a, piece_cnt, st);
+      if (rc != ATTN_OK) return rc;
+      return launch_merge<T, D>(a, o, lse, 0, piece_cnt, st);
     }
-  } else {
-    rc = launch_decode_plain<T, D, PAGED>(a, st);
-    chunk = attn::kPlainChunk;
   }
+  const int rc = launch_decode_plain<T, D, PAGED>(a, st);
   if (rc != ATTN_OK) return rc;
-  return launch_merge<T, D>(a, o, lse, chunk, st);
+  return launch_merge<T, D>(a, o, lse, attn::kPlainChunk, nullptr, st);
 }
 
 template <typename T, bool PAGED>
-int decode_d(const attn::DecodeArgs& a, void* o, float* lse, int d, bool mfma, hipStream_t st) {
+int decode_d(const attn::DecodeArgs& a, void* o, float* lse, int d, bool mfma, int32_t* cnt, hipStream_t st) {
   switch (d) {
-    case 16: return decode_typed<T, 16, PAGED>(a, o, lse, mfma, st);
-    case 32: return decode_typed<T, 32, PAGED>(a, o, lse, mfma, st);
-    case 64: return decode_typed<T, 64, PAGED>(a, o, lse, mfma, st);
-    case 128: return decode_typed<T, 128, PAGED>(a, o, lse, mfma, st);
-    case 256: return decode_typed<T, 256, PAGED>(a, o, lse, mfma, st);
+    case 16: return decode_typed<T, 16, PAGED>(a, o, lse, mfma, cnt, st);
+    case 32: return decode_typed<T, 32, PAGED>(a, o, lse, mfma, cnt, st);
+    case 64: return decode_typed<T, 64, PAGED>(a, o, lse, mfma, cnt, st);
+    case 128: return decode_typed<T, 128, PAGED>(a, o, lse, mfma, cnt, st);
+    case 256: return decode_typed<T, 256, PAGED>(a, o, lse, mfma, cnt, st);
   }
   return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim %d not supported", d);
 }
 
 template <bool PAGED>
-int decode_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, int dtype, float scale,
+int decode_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, int dtype, float scale, int32_t* cnt,
                     hipStream_t st) {
   const bool mfma = mfma_path(dtype, d, scale);
   switch (dtype) {
-    case ATTN_F32: return decode_d<attn::F32, PAGED>(a, o, lse, d, false, st);
-    case ATTN_F16: return decode_d<attn::F16, PAGED>(a, o, lse, d, mfma, st);
-    case ATTN_BF16: return decode_d<attn::BF16, PAGED>(a, o, lse, d, mfma, st);
+    case ATTN_F32: return decode_d<attn::F32, PAGED>(a, o, lse, d, false, cnt, st);
+    case ATTN_F16: return decode_d<attn::F16, PAGED>(a, o, lse, d, mfma, cnt, st);
+    case ATTN_BF16: return decode_d<attn::BF16, PAGED>(a, o, lse, d, mfma, cnt, st);
   }
   return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: dtype %d not supported", dtype);
 }
@@ -294,6 +318,7 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
   if (!aligned16(workspace) || (lse && !aligned16(lse)))
     return fail(ATTN_ERR_INVALID_ARG, "%s: workspace and lse must be 16-byte aligned", fn);
   const int S = splits_for(capacity);
+  const WorkspaceLayout lay = workspace_layout(B, H_q, capacity, d);
   attn::DecodeArgs a;
   a.q = q;
   a.k = k;
@@ -301,8 +326,7 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
   a.table = table;
   a.seq_lens = seq_lens;
   a.part_o = static_cast<float*>(workspace);
-  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        align_up((size_t)B * H_q * S * d * sizeof(float), 256));
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off);
   a.B = B;
   a.H_q = H_q;
   a.H_kv = H_kv;
@@ -311,9 +335,10 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
   a.num_blocks = num_blocks;
   a.s_max = S;
   a.scale_log2 = scale * attn::kLog2e;
+  int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.cnt_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return paged ? decode_dispatch<true>(a, o, lse, d, dtype, scale, st)
-               : decode_dispatch<false>(a, o, lse, d, dtype, scale, st);
+  return paged ? decode_dispatch<true>(a, o, lse, d, dtype, scale, cnt, st)
+               : decode_dispatch<false>(a, o, lse, d, dtype, scale, cnt, st);
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* o,

@@ -133,12 +133,14 @@ struct MergeArgs {
   const float* part_o;
   const float* part_lse;
   const int32_t* seq_lens;
+  const int32_t* piece_cnt;  // [B][H_q] pieces per segment, or nullptr: ceil(len / chunk) splits
   void* o;          // [B, H_q, d]
   float* lse;       // [B, H_q] or nullptr
   int H_q;
   int capacity;
   int s_max;
-  int chunk;        // tokens per split
+  int chunk;        // tokens per split (piece_cnt == nullptr)
+  int G, n_hg;      // query heads per KV head, groups of 16 of them (piece_cnt != nullptr)
 };
 
 // Combine the split partials of one (sequence, query head): one wave, lanes
@@ -152,7 +154,14 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x;
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > a.capacity ? a.capacity : len);
-  const int ns = (len + a.chunk - 1) / a.chunk;
+  int ns;
+  if (a.piece_cnt == nullptr) {
+    ns = (len + a.chunk - 1) / a.chunk;
+  } else {
+    const int gh = (h / a.G) * a.n_hg + (h % a.G) / 16;  // segment of this query head
+    ns = len == 0 ? 0 : a.piece_cnt[(size_t)b * a.H_q + gh];
+    ns = ns < 0 ? 0 : (ns > a.s_max ? a.s_max : ns);
+  }
   const size_t base = ((size_t)b * a.H_q + h) * a.s_max;
   float M = kNegInf;
   for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.part_lse[base + s]);
