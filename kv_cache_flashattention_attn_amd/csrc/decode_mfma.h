@@ -14,10 +14,12 @@
 // end, form one stream; the grid is a fixed number of waves (as many as fit
 // on the GPU at once) and wave k takes an equal contiguous share of the
 // stream.  A wave never waits for another:
-//  * stage copies go straight from global memory into a wave-private LDS ring
-//    of kDecSlots stages (global_load_lds_dwordx4), the next one in flight
-//    while the current one is computed, across segment boundaries; the query
-//    rows of a segment ride along with its first stage;
+//  * each stage's K rows are loaded straight into MFMA operand registers and
+//    its V rows into registers, the next stage's loads in flight while the
+//    current one is computed, across segment boundaries (plain 16-byte loads:
+//    they stream faster than global-to-LDS copies on this part); the query
+//    rows of a segment are loaded with its first stage;
+//  * V goes through a 4 KB wave-private LDS tile to be read transposed;
 //  * S^T = K Q^T with v_mfma_f32_16x16x32 (16 tokens x 16 query heads, heads
 //    beyond G are don't-care columns), K rows read with ds_read_b128;
 //  * running (max, sum) per head; the reference maximum only moves when a
@@ -36,8 +38,7 @@
 namespace attn {
 
 constexpr int kDecStage = 16;     // tokens per stage (one cache block)
-constexpr int kDecSlots = 2;      // ring stages per wave
-constexpr int kDecWaves = 2;      // waves per workgroup
+constexpr int kDecWaves = 4;      // waves per workgroup
 constexpr int kDecMinShare = 16;  // stages per wave at least (bounds the pieces per segment)
 
 // Pieces a segment of at most `capacity` tokens can be cut into.
@@ -71,19 +72,14 @@ __device__ __forceinline__ f32x4 mfma16k16<F16>(i16x4 a, u32x2 b, f32x4 c) {
                                                0, 0, 0);
 }
 
-// Geometry of 16 rows (of K, V or Q; 16-bit elements) in LDS.
+// Geometry of one V stage (16 rows, 16-bit elements) in LDS.
 template <int D>
 struct DecGeom {
   static constexpr int ROWB = D * 2;                 // bytes per row
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int RPL = 256 / ROWB;             // rows per 256-byte bank line (1 or 2)
   static constexpr int SLOT = kDecStage * ROWB;      // bytes of 16 rows
-  static constexpr int COPIES = SLOT / 1024;         // wave-wide 1 KB copies per 16 rows
-  static constexpr int ROWS_PER_COPY = 1024 / ROWB;
-  // per wave: kDecSlots x (K, V) stages, then kDecSlots query slots
-  static constexpr int WAVE_LDS = kDecSlots * 3 * SLOT;
-  // K and Q operand reads: 16 lanes read 16 consecutive rows at one logical chunk.
-  static __device__ __forceinline__ int swz_k(int r) { return (r / RPL) % CH; }
+  static constexpr int VCH = SLOT / 16 / 64;         // 16-byte chunks of V per lane per stage
   // V transposing read: a half-wave reads 8 consecutive rows at chunks {2m, 2m+1}.
   static __device__ __forceinline__ int swz_v(int r) { return 2 * ((r / RPL) % (CH / 2)); }
 };
@@ -111,16 +107,14 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   using Gm = DecGeom<D>;
   constexpr int KS = D / 32;   // 32-deep k-steps of Q K^T
   constexpr int DB = D / 16;   // 16-wide blocks of d
-  constexpr int ROWB = Gm::ROWB, CH = Gm::CH;
-  constexpr int NCP = 2 * Gm::COPIES;  // copies per stage (K and V)
-  constexpr int kQBase = kDecSlots * 2 * Gm::SLOT;  // query slots follow the K/V stages
+  constexpr int ROWB = Gm::ROWB, VCH = Gm::VCH;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kDecWaves * Gm::WAVE_LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t vtile[kDecWaves * Gm::SLOT];
 
   const DecodeArgs& a = sa.a;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
-  const int col = l & 15, grp = l >> 4;   // MFMA column (head) and k-group
+  const int col = l & 15, grp = l >> 4;   // MFMA column (head / token row) and k-group
   const int G = a.H_q / a.H_kv;
   const int GH = a.H_kv * sa.n_hg;        // segments per sequence
   const int worker = blockIdx.x * kDecWaves + w;
@@ -183,7 +177,6 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       pre += __builtin_amdgcn_readlane(incl, 63);
     }
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the lengths above have landed before any stage copy
 
   auto advance = [&](Cursor& c) {
     ++c.pos;
@@ -197,76 +190,61 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       c.n = stages_of(c.len);
     } while (c.n == 0);
   };
-  // a segment's first stage in this wave's share: the query rows come with it
+  // a segment's first stage in this wave's share: its query rows are loaded with it
   auto seg_start = [&](const Cursor& c) { return c.st == 0 || c.pos == beg; };
 
   const uint8_t* kp = static_cast<const uint8_t*>(a.k);
   const uint8_t* vp = static_cast<const uint8_t*>(a.v);
-  const uint8_t* qp = static_cast<const uint8_t*>(a.q);
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const float c_log2 = a.scale_log2;  // > 0 on this path
+  uint8_t* vt = vtile + w * Gm::SLOT;
 
-  // lane offsets of the wave-wide copies: copy i fills rows i * ROWS_PER_COPY + l / CH
-  uint32_t koff[Gm::COPIES], voff[Gm::COPIES];
-#pragma unroll
-  for (int i = 0; i < Gm::COPIES; ++i) {
-    const int r = i * Gm::ROWS_PER_COPY + l / CH;
-    koff[i] = r * ROWB + 16 * ((l % CH) ^ Gm::swz_k(r));
-    voff[i] = r * ROWB + 16 * ((l % CH) ^ Gm::swz_v(r));
-  }
-  const uint32_t wave_lds = lds_addr(ring) + w * Gm::WAVE_LDS;
-  const uint8_t* wave_ring = ring + w * Gm::WAVE_LDS;
-
-  // Block id of the stage under cursor c (paged).  Read one stage ahead of its
-  // copies, so that the scalar load's latency hides behind the wait for the
-  // stage being computed.
-  auto block_of = [&](const Cursor& c) {
-    return (PAGED && c.pos < end) ? table[(int64_t)c.b * a.max_blocks_per_seq + c.st] : 0;
+  // One stage in registers: K rows in MFMA operand layout (lane -> token row
+  // col, 16 bytes at d = 32 ks + 8 grp), V rows as loaded (lane -> row l / 4,
+  // 64 bytes at byte 64 (l % 4)), and the query fragments when the stage
+  // starts a segment.
+  struct Stage {
+    u32x4 k[KS];
+    u32x4 v[VCH];
+    u32x4 q[KS];
+    bool ok;     // valid block id (paged)
+    bool qnew;   // q holds a new segment's query rows
   };
-
-  // Issue the copies of the stage under cursor c (paged: in block blk) into
-  // ring slot `slot` (query rows first when it starts a segment, into query
-  // slot `qslot`).  Returns false for an invalid block id: block 0 is copied
-  // instead (so every stage issues the same copies) and the stage is masked.
-  auto issue = [&](const Cursor& c, int blk, int slot, int qslot) -> bool {
+  // K and V loads come first and are unconditional (same count on every
+  // path, so the compiler's vmcnt waits stay exact); query rows follow only
+  // when the stage starts a segment.
+  // Paged: block id of the stage under cursor c, read one stage before its
+  // loads so the scalar load's latency hides behind the current stage.
+  auto block_of = [&](const Cursor& c) {
+    return PAGED ? table[(int64_t)c.b * a.max_blocks_per_seq + c.st] : 0;
+  };
+  auto load = [&](const Cursor& c, const int blk, Stage& S) {
     const int g = c.gh / sa.n_hg, hg = c.gh % sa.n_hg;
-    if (seg_start(c)) {
-      // rows of query heads g*G + 16 hg + r (rows past the group repeat head g*G)
-      const uint32_t qdst = wave_lds + kQBase + qslot * Gm::SLOT;
-#pragma unroll
-      for (int i = 0; i < Gm::COPIES; ++i) {
-        const int r = i * Gm::ROWS_PER_COPY + l / CH;
-        const int gi = 16 * hg + r;
-        const size_t row = (size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0);
-        lds_copy16(qp + row * ROWB + 16 * ((l % CH) ^ Gm::swz_k(r)), qdst + i * 1024);
-      }
-    }
-    const uint32_t kdst = wave_lds + slot * 2 * Gm::SLOT;
-    const uint32_t vdst = kdst + Gm::SLOT;
-    bool valid = true;
     size_t row0;
+    S.ok = true;
     if (PAGED) {
-      valid = blk >= 0 && blk < a.num_blocks;
-      row0 = ((size_t)(valid ? blk : 0) * a.H_kv + g) * kDecStage;
+      S.ok = blk >= 0 && blk < a.num_blocks;
+      row0 = ((size_t)(S.ok ? blk : 0) * a.H_kv + g) * kDecStage;
     } else {
       row0 = ((size_t)c.b * a.H_kv + g) * a.capacity + (size_t)c.st * kDecStage;
     }
-    if (PAGED || (c.st + 1) * kDecStage <= a.capacity) {
+    // contiguous: rows past the capacity (last stage only) read the last row instead
+    const int kr = PAGED ? col : min(col, a.capacity - 1 - c.st * kDecStage);
+    const int vr = PAGED ? (l >> 2) : min(l >> 2, a.capacity - 1 - c.st * kDecStage);
+    const uint8_t* ks_src = kp + (row0 + kr) * ROWB + 16 * grp;
 #pragma unroll
-      for (int i = 0; i < Gm::COPIES; ++i) {
-        lds_copy16(kp + row0 * ROWB, koff[i], kdst + i * 1024);
-        lds_copy16(vp + row0 * ROWB, voff[i], vdst + i * 1024);
-      }
-    } else {  // rows past the capacity are clamped to the last row (and masked)
+    for (int ks = 0; ks < KS; ++ks) S.k[ks] = *reinterpret_cast<const u32x4*>(ks_src + 64 * ks);
+    const uint8_t* vs_src = vp + (row0 + vr) * ROWB + (ROWB / 4) * (l & 3);
 #pragma unroll
-      for (int i = 0; i < Gm::COPIES; ++i) {
-        const int r = i * Gm::ROWS_PER_COPY + l / CH;
-        const int t = c.st * kDecStage + r;
-        const ptrdiff_t shift = (ptrdiff_t)(min(t, a.capacity - 1) - t) * ROWB;
-        lds_copy16(kp + row0 * ROWB + koff[i] + shift, kdst + i * 1024);
-        lds_copy16(vp + row0 * ROWB + voff[i] + shift, vdst + i * 1024);
-      }
+    for (int i = 0; i < VCH; ++i) S.v[i] = *reinterpret_cast<const u32x4*>(vs_src + 16 * i);
+    S.qnew = seg_start(c);
+    if (S.qnew) {
+      // query heads g*G + 16 hg + col (columns past the group repeat head g*G)
+      const int gi = 16 * hg + col;
+      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + 32 * ks);
     }
-    return valid;
   };
 
   // per-segment state
@@ -296,71 +274,38 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     }
   };
 
-  Cursor cc = ic;                // stage to compute; ic = next stage to issue
-  int q_issued = 0, q_used = 0;  // query slots issued / consumed (ring of kDecSlots)
-  unsigned ok_bits = 0;          // bit `slot`: that ring slot holds a valid block
-  unsigned qs_bits = 0;          // bit `slot`: the stage in that slot also brought query rows
-  static_assert(kDecSlots == 2, "the wait counts below assume two slots");
-  int ic_blk = block_of(ic);
-  for (int s = 0; s < kDecSlots && ic.pos < end; ++s) {
-    const bool q = seg_start(ic);
-    if (issue(ic, ic_blk, s, q_issued % kDecSlots)) ok_bits |= 1u << s;
-    if (q) {
-      qs_bits |= 1u << s;
-      ++q_issued;
-    }
-    advance(ic);
-    ic_blk = block_of(ic);
-  }
-
-  for (int pos = beg; pos < end; ++pos) {
-    const int slot = (pos - beg) % kDecSlots;
-    // wait until only the next stage's copies are outstanding
-    if (pos + 1 < end) {
-      if ((qs_bits >> (slot ^ 1)) & 1u)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NCP + Gm::COPIES));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NCP));
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    }
-    const bool ok = (ok_bits >> slot) & 1u;
-    if (!ok && l == 0) raise_device_error(2);
-    if (seg_start(cc)) {
-      const uint8_t* Qs = wave_ring + kQBase + (q_used % kDecSlots) * Gm::SLOT;
-      ++q_used;
+  auto compute = [&](const Cursor& c, const Stage& S, const bool last) {
+    if (!S.ok && l == 0) raise_device_error(2);
+    if (S.qnew) {
+      // New segment.  O is not cleared here: with m = -inf the first stage
+      // that sees a finite score rescales it by exp2(-inf) = 0.
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = (4 * ks + grp) ^ Gm::swz_k(col);
-        qf[ks] = *reinterpret_cast<const u32x4*>(Qs + col * ROWB + 16 * ch);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = S.q[ks];
       m = kNegInf;
       lsum = 0.f;
       lexact = 0.f;
       // piece p of a segment belongs to the p-th wave whose share overlaps it
-      const int seg0 = cc.pos - cc.st;
+      const int seg0 = c.pos - c.st;
       piece = worker - seg0 / share;
       if (piece == 0 && l == 0)
-        sa.piece_cnt[(size_t)cc.b * a.H_q + cc.gh] = (seg0 + cc.n - 1) / share - seg0 / share + 1;
+        sa.piece_cnt[(size_t)c.b * a.H_q + c.gh] = (seg0 + c.n - 1) / share - seg0 / share + 1;
     }
-    const uint8_t* Ks = wave_ring + slot * 2 * Gm::SLOT;
-    const uint8_t* Vs = Ks + Gm::SLOT;
-    const int t0 = cc.st * kDecStage;
-
+    // V rows into the LDS tile (row l / 4, logical chunks VCH (l % 4) + i)
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int r = l >> 2;
+      const int ch = (VCH * (l & 3) + i) ^ Gm::swz_v(r);
+      *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ch) = S.v[i];
+    }
     // S^T = K Q^T: lane holds head col, tokens t0 + 4 grp + i
+    const int t0 = c.st * kDecStage;
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = (4 * ks + grp) ^ Gm::swz_k(col);
-      const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + col * ROWB + 16 * ch);
-      sacc = mfma16k32<T>(kf, qf[ks], sacc);
-    }
-    if (!ok || t0 + kDecStage > cc.len) {
+    for (int ks = 0; ks < KS; ++ks) sacc = mfma16k32<T>(S.k[ks], qf[ks], sacc);
+    if (!S.ok || t0 + kDecStage > c.len) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (!ok || t0 + 4 * grp + i >= cc.len) sacc[i] = kNegInf;
+        if (!S.ok || t0 + 4 * grp + i >= c.len) sacc[i] = kNegInf;
     }
     float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     tmax = fmaxf(tmax, xor_shfl(tmax, 16));
@@ -383,35 +328,51 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     const u32x2 pf = u32x2{cvt_pk<T>(p[0], p[1]), cvt_pk<T>(p[2], p[3])};
     lsum = add_pair<T>(pf[1], add_pair<T>(pf[0], lsum));
     lexact += (p[0] + p[1]) + (p[2] + p[3]);
-
-    // O^T += V^T P^T
+    // O^T += V^T P^T (the wave's own LDS writes above precede these reads)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int ch = ((16 * db + 4 * vq) >> 3) ^ Gm::swz_v(vrow);
       const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(Vs + vrow * ROWB + 16 * ch + 2 * ((4 * vq) & 7)));
+          (lds_i16x4*)(vt + vrow * ROWB + 16 * ch + 2 * ((4 * vq) & 7)));
       oacc[db] = mfma16k16<T>(vf, pf, oacc[db]);
     }
+    if (c.st + 1 == c.n || last) finish(c);
+  };
 
-    if (cc.st + 1 == cc.n || pos + 1 == end) finish(cc);
-    // refill this slot with the stage kDecSlots ahead
-    if (ic.pos < end) {
-      __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);  // this slot's reads are done
-      const bool q = seg_start(ic);
-      const bool valid = issue(ic, ic_blk, slot, q_issued % kDecSlots);
-      ok_bits = valid ? (ok_bits | 1u << slot) : (ok_bits & ~(1u << slot));
-      if (q) {
-        qs_bits |= 1u << slot;
-        ++q_issued;
-      } else {
-        qs_bits &= ~(1u << slot);
-      }
+  // two stages in registers: compute one while the next one's loads are in
+  // flight.  Past the end of the share the loads repeat the current stage
+  // (never used), so every iteration issues the same loads.
+  Cursor cc = ic;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // nblk: block id of stage ic (the dummy reloads past the end reuse it; load
+  // checks every id it is given)
+  Stage A, B;
+  int nblk = block_of(ic);
+  load(ic, nblk, A);
+  advance(ic);
+  if (ic.pos < end) nblk = block_of(ic);
+  for (int pos = beg; pos < end; pos += 2) {
+    if (pos + 1 < end) {
+      load(ic, nblk, B);
       advance(ic);
-      ic_blk = block_of(ic);
+      if (ic.pos < end) nblk = block_of(ic);
+    } else {
+      load(cc, nblk, B);
     }
+    compute(cc, A, pos + 1 == end);
+    advance(cc);
+    if (pos + 1 >= end) break;
+    if (pos + 2 < end) {
+      load(ic, nblk, A);
+      advance(ic);
+      if (ic.pos < end) nblk = block_of(ic);
+    } else {
+      load(cc, nblk, A);
+    }
+    compute(cc, B, pos + 2 == end);
     advance(cc);
   }
-  (void)CH;
 }
 
 }  // namespace attn
