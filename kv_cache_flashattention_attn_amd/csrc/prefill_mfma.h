@@ -34,10 +34,10 @@
 //    O accumulator is rescaled on a few tiles only, not on every tile.
 //  * Workgroup order: the hardware deals workgroup ids round-robin to the 8
 //    XCDs, each with its own L2.  Ids are remapped so that XCD x runs a
-//    contiguous range of (batch, head) pairs, all query tiles of one head
-//    back to back: an XCD works on about two heads at a time and their K/V
-//    (2 MB at N = 4096, d = 128) stays in its 4 MB L2.  Within a head the
-//    longest causal tiles go first.
+//    contiguous range of (batch, head) pairs a few heads at a time, so their
+//    K/V (2 MB per head at N = 4096, d = 128) is mostly served from L2.
+//    Causal query blocks run longest first across each group of heads (see
+//    prefill_block_order).
 #pragma once
 #include "mfma_common.h"
 #include "prefill_plain.h"
@@ -84,6 +84,37 @@ struct PrefillGeom {
   static __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) % (CH / 4)); }
 };
 
+// Workgroup order: (batch x head, query block) of workgroup `bid`.
+// The hardware deals ids round-robin to the 8 XCDs (XCD x runs x, x + 8, ...),
+// and each XCD is given a contiguous range of (b, h) pairs, so that their K/V
+// stay in its own L2.  Causal query blocks differ in length (the last block of
+// a head does n_qt times the work of the first), so within each group of
+// kHeadGroup heads of that range the blocks run longest first across the
+// group: the last blocks the GPU starts are the shortest ones and the CUs
+// finish together.
+constexpr int kHeadGroup = 4;
+__device__ __forceinline__ void prefill_block_order(int bid, int n_qt, int total, bool causal, int& bh, int& qt) {
+  if (total % kNumXcd == 0) {
+    const int per_xcd = total / kNumXcd;  // workgroups per XCD
+    const int k = bid / kNumXcd;          // position within this XCD
+    const int base = (bid % kNumXcd) * per_xcd;
+    if (causal && per_xcd % n_qt == 0) {
+      const int heads = per_xcd / n_qt;
+      const int hg = heads % kHeadGroup == 0 ? kHeadGroup : (heads % 2 == 0 ? 2 : 1);
+      const int gi = k / (hg * n_qt), j = k % (hg * n_qt);
+      bh = base / n_qt + gi * hg + j % hg;
+      qt = n_qt - 1 - j / hg;
+      return;
+    }
+    const int t = base + k;
+    bh = t / n_qt;
+    qt = causal ? n_qt - 1 - t % n_qt : t % n_qt;
+    return;
+  }
+  bh = bid / n_qt;
+  qt = causal ? n_qt - 1 - bid % n_qt : bid % n_qt;
+}
+
 template <typename T, int D, int NW, bool CAUSAL, bool LSE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 prefill_mfma_kernel(PrefillArgs a) {
@@ -102,10 +133,8 @@ prefill_mfma_kernel(PrefillArgs a) {
   const int BH = a.B * a.H_q;
   const int n_qt = (a.N + BM - 1) / BM;
   const int total = n_qt * BH;
-  const int bid = blockIdx.x;
-  const int t = (total % kNumXcd == 0) ? (bid % kNumXcd) * (total / kNumXcd) + bid / kNumXcd : bid;
-  const int bh = t / n_qt;
-  const int qt = CAUSAL ? (n_qt - 1 - t % n_qt) : (t % n_qt);
+  int bh, qt;
+  prefill_block_order(blockIdx.x, n_qt, total, CAUSAL, bh, qt);
   const int b = bh / a.H_q, h = bh % a.H_q;
   const int g = h / (a.H_q / a.H_kv);
   const int q0 = qt * BM;
