@@ -153,6 +153,41 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       int max_blocks_per_seq, int num_blocks, float scale, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_prefill_paged -- a chunk of n_new queries per sequence against a paged
+ * KV cache that already holds the chunk's own keys (chunked prefill, prefix
+ * reuse).
+ *
+ * The KV cache exists so that the keys and values of tokens already processed
+ * are never recomputed ("推理速度慢怎么办？..." section 一; "KV Cache:推理慢的真正原因",
+ * 为什么需要 KV Cache); here a block of new tokens attends to that cached
+ * prefix plus itself, using the same block table as decode
+ * ("KV Cache:推理慢的真正原因", 工程优化手段 / 1. PagedAttention).  Call
+ * kv_append with the chunk's K/V first.
+ *
+ *   q, o        : [B, H_q, n_new, d]; query t of sequence b is token
+ *                 cache_lens[b] + t.
+ *   k_pool, v_pool : [num_blocks, H_kv, block_size, d], block_size == 16.
+ *   block_table : device int32 [B, max_blocks_per_seq], as for attn_decode_paged.
+ *   cache_lens  : device int32 [B], tokens cached BEFORE the chunk; sequence b
+ *                 has cache_lens[b] + n_new keys.
+ *   causal != 0 : query t sees keys 0 .. cache_lens[b] + t; otherwise all
+ *                 cache_lens[b] + n_new keys.
+ *   lse         : [B, H_q, n_new] fp32 or NULL.
+ * f16/bf16 at d = 64 or 128, scale > 0 (the MFMA path).  A length outside
+ * [0, max_blocks_per_seq * 16 - n_new] is clamped and raises
+ * ATTN_DEVERR_LEN_OVERFLOW / ATTN_DEVERR_BAD_LEN; a block id outside
+ * [0, num_blocks) reads block 0 (its keys' contribution is then unspecified)
+ * and raises ATTN_DEVERR_BAD_BLOCK.
+ * Errors: INVALID_ARG, UNSUPPORTED (dtype, d, block_size, scale <= 0), HIP.
+ */
+int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* cache_lens,
+                       void* o, float* lse,
+                       int B, int H_q, int H_kv, int n_new, int d, int block_size,
+                       int max_blocks_per_seq, int num_blocks, int causal, float scale,
+                       int dtype, void* stream);
+
 /* Workspace bytes attn_decode / attn_decode_paged need for a cache capacity of
  * max_seq_len tokens per sequence.  0 on invalid sizes. */
 size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d);

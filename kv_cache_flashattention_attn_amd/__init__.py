@@ -21,7 +21,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "AttnError", "lib", "lib_path", "attn_prefill", "kv_append", "attn_decode", "attn_decode_paged",
+    "AttnError", "lib", "lib_path", "attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode",
+    "attn_decode_paged",
     "attn_decode_workspace_bytes", "attn_device_error_flags", "attn_version", "DTYPE_CODES",
     "EXPORTED_SYMBOLS",
 ]
@@ -33,7 +34,7 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
           4: "ATTN_ERR_HIP"}
-EXPORTED_SYMBOLS = ("attn_prefill", "kv_append", "attn_decode", "attn_decode_paged",
+EXPORTED_SYMBOLS = ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
                     "attn_decode_workspace_bytes", "attn_last_error", "attn_version",
                     "attn_device_error_flags")
 
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(lib_path)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    L.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                     i32, vp]
     L.kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp]
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
@@ -67,7 +70,8 @@ def lib() -> ctypes.CDLL:
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_version.restype = ctypes.c_char_p
     L.attn_device_error_flags.argtypes = [vp]
-    for name in ("attn_prefill", "kv_append", "attn_decode", "attn_decode_paged", "attn_device_error_flags"):
+    for name in ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
+                 "attn_device_error_flags"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -120,6 +124,32 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
                             B, H_q, H_kv, N, d, int(bool(causal)), scale, _code(q), int(bool(out_fp32)),
                             _stream())
     _check("attn_prefill", rc)
+    return (out, lse) if return_lse else out
+
+
+def attn_prefill_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+                       cache_lens: torch.Tensor, causal: bool = True, scale: Optional[float] = None,
+                       return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None):
+    """Chunk of n_new queries per sequence, q [B, H_q, n_new, d], against paged pools
+    [num_blocks, H_kv, 16, d] that already hold the chunk's keys (query t of sequence b
+    is token cache_lens[b] + t)."""
+    B, H_q, n_new, d = q.shape
+    nb, H_kv, bs, _ = k_pool.shape
+    if v_pool.shape != k_pool.shape or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise ValueError("k_pool and v_pool must match each other and q's dtype")
+    mbps = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q, n_new), dtype=torch.float32, device=q.device)
+    rc = lib().attn_prefill_paged(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                  _dev(block_table, "block_table", torch.int32),
+                                  _dev(cache_lens, "cache_lens", torch.int32), _dev(out, "out"),
+                                  _dev(lse, "lse", torch.float32) if return_lse else 0,
+                                  B, H_q, H_kv, n_new, d, bs, mbps, nb, int(bool(causal)), scale, _code(q),
+                                  _stream())
+    _check("attn_prefill_paged", rc)
     return (out, lse) if return_lse else out
 
 

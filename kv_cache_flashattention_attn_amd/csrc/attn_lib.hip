@@ -117,8 +117,9 @@ int prefill_plain_d(const attn::PrefillArgs& a, int d, bool causal, hipStream_t 
   return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not supported", d);
 }
 
-template <typename T, int D>
-int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st) {
+template <typename T, int D, bool PAGED>
+int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st, const attn::PagedKV& pk = {0, 0},
+                        const int32_t* table = nullptr, const int32_t* cache_lens = nullptr) {
   constexpr int NW = attn::kPrefillWaves;
   const long long n_qt = (a.N + 32 * NW - 1) / (32 * NW);
   const long long blocks = n_qt * a.B * a.H_q;
@@ -126,19 +127,30 @@ int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st)
   const dim3 grid((unsigned)blocks), block(64 * NW);
   const bool lse = a.lse != nullptr;
   if (causal && lse)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, true, PAGED>), grid, block, 0, st, a, pk, table,
+                       cache_lens);
   else if (causal)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, false, PAGED>), grid, block, 0, st, a, pk, table,
+                       cache_lens);
   else if (lse)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, true, PAGED>), grid, block, 0, st, a, pk, table,
+                       cache_lens);
   else
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, false, PAGED>), grid, block, 0, st, a, pk, table,
+                       cache_lens);
   return launch_status("attn_prefill");
 }
 
 template <typename T>
 int prefill_mfma_d(const attn::PrefillArgs& a, int d, bool causal, hipStream_t st) {
-  return d == 64 ? launch_prefill_mfma<T, 64>(a, causal, st) : launch_prefill_mfma<T, 128>(a, causal, st);
+  return d == 64 ? launch_prefill_mfma<T, 64, false>(a, causal, st) : launch_prefill_mfma<T, 128, false>(a, causal, st);
+}
+
+template <typename T>
+int prefill_paged_d(const attn::PrefillArgs& a, int d, bool causal, const attn::PagedKV& pk, const int32_t* table,
+                    const int32_t* cache_lens, hipStream_t st) {
+  return d == 64 ? launch_prefill_mfma<T, 64, true>(a, causal, st, pk, table, cache_lens)
+                 : launch_prefill_mfma<T, 128, true>(a, causal, st, pk, table, cache_lens);
 }
 
 // ---------------------------------------------------------------------------
@@ -256,6 +268,41 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
     case ATTN_F16: return prefill_plain_d<attn::F16>(a, d, c, st);
     default: return prefill_plain_d<attn::BF16>(a, d, c, st);
   }
+}
+
+int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                       const int32_t* cache_lens, void* o, float* lse, int B, int H_q, int H_kv, int n_new, int d,
+                       int block_size, int max_blocks_per_seq, int num_blocks, int causal, float scale, int dtype,
+                       void* stream) {
+  if (!q || !k_pool || !v_pool || !block_table || !cache_lens || !o)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: null pointer");
+  if (B < 1 || H_q < 1 || H_kv < 1 || n_new < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: B, H_q, H_kv, n_new must be >= 1");
+  if (H_q % H_kv != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: H_q (%d) is not a multiple of H_kv (%d)", H_q, H_kv);
+  if (B > 65535 || H_q > 65535) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: B or H_q too large");
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_paged: block_size must be 16 (got %d)", block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: max_blocks_per_seq and num_blocks must be >= 1");
+  if ((long long)max_blocks_per_seq * 16 > 0x7FFFFFFFLL || (long long)max_blocks_per_seq * B > 0x7FFFFFFFLL)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: block table too large");
+  if (n_new > max_blocks_per_seq * 16)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: n_new (%d) exceeds the table's capacity (%d)", n_new,
+                max_blocks_per_seq * 16);
+  if (!(dtype == ATTN_F16 || dtype == ATTN_BF16) || !(d == 64 || d == 128))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_paged: f16/bf16 with d = 64 or 128 only");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_paged: scale must be finite and positive");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: tensors must be 16-byte aligned");
+  if ((long long)n_new * d > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_paged: n_new*d too large");
+
+  attn::PrefillArgs a{q, k_pool, v_pool, o, lse, B, H_q, H_kv, n_new, scale * attn::kLog2e, 0};
+  const attn::PagedKV pk{max_blocks_per_seq, num_blocks};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return dtype == ATTN_BF16 ? prefill_paged_d<attn::BF16>(a, d, causal != 0, pk, block_table, cache_lens, st)
+                            : prefill_paged_d<attn::F16>(a, d, causal != 0, pk, block_table, cache_lens, st);
 }
 
 int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* cache_lens,

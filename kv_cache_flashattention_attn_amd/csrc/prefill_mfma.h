@@ -115,9 +115,20 @@ __device__ __forceinline__ void prefill_block_order(int bid, int n_qt, int total
   qt = causal ? n_qt - 1 - bid % n_qt : bid % n_qt;
 }
 
-template <typename T, int D, int NW, bool CAUSAL, bool LSE>
+// Keys and values of a paged cache (chunked prefill): pools
+// [num_blocks, H_kv, 16, d], token p of sequence b in block
+// table[b * max_blocks_per_seq + p / 16], row p % 16; the N queries of
+// sequence b sit at positions cache_lens[b] .. cache_lens[b] + N - 1 (their
+// keys already appended), so it has cache_lens[b] + N keys.
+struct PagedKV {
+  int max_blocks_per_seq;
+  int num_blocks;
+};
+
+template <typename T, int D, int NW, bool CAUSAL, bool LSE, bool PAGED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
-prefill_mfma_kernel(PrefillArgs a) {
+prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table,
+                    const int32_t* __restrict__ cache_lens) {
   using Gm = PrefillGeom<D, NW>;
   constexpr int BM = Gm::BM, BN = Gm::BN, ROWB = Gm::ROWB, CH = Gm::CH, TILE = Gm::TILE;
   constexpr int KS = D / 16;  // 16-deep k-steps of Q K^T
@@ -145,12 +156,23 @@ prefill_mfma_kernel(PrefillArgs a) {
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* vp = static_cast<const uint16_t*>(a.v);
-  const size_t kv_base = ((size_t)b * a.H_kv + g) * (size_t)a.N * D;
+  const size_t kv_base = PAGED ? 0 : ((size_t)b * a.H_kv + g) * (size_t)a.N * D;
 
-  const int key_end = CAUSAL ? min(a.N, q0 + BM) : a.N;
+  // Nk keys; query row i sits at key position off + i
+  int off = 0;
+  if (PAGED) {
+    off = cache_lens[b];
+    const int room = pk.max_blocks_per_seq * 16 - a.N;  // >= 0 (checked on the host)
+    if (off < 0 || off > room) {
+      if (tid == 0) raise_device_error(off < 0 ? 4 : 1);
+      off = off < 0 ? 0 : room;
+    }
+  }
+  const int Nk = off + a.N;
+  const int key_end = CAUSAL ? min(Nk, off + q0 + BM) : Nk;
   const int n_kt = (key_end + BN - 1) / BN;
   // tiles every row of the workgroup sees in full (no mask, no skip)
-  const int n_full = CAUSAL ? min((q0 + 1) / BN, a.N / BN) : a.N / BN;
+  const int n_full = CAUSAL ? min((off + q0 + 1) / BN, Nk / BN) : Nk / BN;
   const uint32_t smem_base = lds_addr(&smem[0][0][0]);
 
   // global -> LDS copy of one K and one V tile: copy i of this wave fills the
@@ -162,7 +184,39 @@ prefill_mfma_kernel(PrefillArgs a) {
   const uint32_t voff = r0 * ROWB + 16 * ((l % CH) ^ Gm::swz_v(r0));
   constexpr int kCopyStride = NW * 1024;  // bytes between consecutive copies of a wave
   // one tensor's tile: src = K or V, off = its lane offset, which = 0 (K) / 1 (V)
+  // paged: the chunk offset of this lane's 16 bytes within its row
+  const uint32_t kch = 16 * ((l % CH) ^ Gm::swz_k(r0)), vch = 16 * ((l % CH) ^ Gm::swz_v(r0));
+  // block id of key position p (an id outside the pool reads block 0 and raises a flag)
+  auto block_at = [&](int p) {
+    int blk = table[(size_t)b * pk.max_blocks_per_seq + (p >> 4)];
+    if (blk < 0 || blk >= pk.num_blocks) {
+      if (l == 0) raise_device_error(2);
+      blk = 0;
+    }
+    return blk;
+  };
+  auto issue_paged = [&](const uint16_t* src, const uint32_t ch, int which, int k0, int buf) {
+    const uint32_t dst = smem_base + (2 * buf + which) * TILE + w * 1024;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(src);
+    const int last = Nk - 1;
+    const int blk_last = block_at(last);
+#pragma unroll
+    for (int i = 0; i < Gm::COPIES; ++i) {
+      // the copy's ROWS_PER_COPY rows lie in one 16-row block; rows past the
+      // last key read the last key instead
+      const int fr = k0 + w * Gm::ROWS_PER_COPY + i * NW * Gm::ROWS_PER_COPY;
+      const int blk = fr <= last ? block_at(fr) : blk_last;
+      const int r = fr + l / CH;
+      const bool in = r <= last;
+      const size_t row = ((size_t)(in ? blk : blk_last) * a.H_kv + g) * 16 + ((in ? r : last) & 15);
+      lds_copy16(base + row * ROWB + ch, dst + i * kCopyStride);
+    }
+  };
   auto issue = [&](const uint16_t* src, const uint32_t off, int which, int k0, int buf) {
+    if (PAGED) {
+      issue_paged(src, which ? vch : kch, which, k0, buf);
+      return;
+    }
     const uint32_t dst = smem_base + (2 * buf + which) * TILE + w * 1024;
     const uint8_t* tile_base = reinterpret_cast<const uint8_t*>(src + kv_base + (size_t)k0 * D);
     if (k0 + BN <= a.N) {
@@ -180,6 +234,10 @@ prefill_mfma_kernel(PrefillArgs a) {
   auto issue_k = [&](int k0, int buf) { issue(kp, koff, 0, k0, buf); };
   auto issue_v = [&](int k0, int buf) { issue(vp, voff, 1, k0, buf); };
   auto issue_v_full = [&](int k0, int buf) {  // a tile known to lie inside the sequence
+    if (PAGED) {
+      issue_paged(vp, vch, 1, k0, buf);
+      return;
+    }
     const uint32_t dst = smem_base + (2 * buf + 1) * TILE + w * 1024;
     const uint8_t* tile_base = reinterpret_cast<const uint8_t*>(vp + kv_base + (size_t)k0 * D);
 #pragma unroll
@@ -234,7 +292,7 @@ prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * rb + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const bool vis = key < a.N && (!CAUSAL || key <= qi);
+          const bool vis = key < Nk && (!CAUSAL || key <= off + qi);
           if (!vis) sacc[rb][i] = kNegInf;
         }
     }
@@ -302,7 +360,7 @@ prefill_mfma_kernel(PrefillArgs a) {
   // P V of tile j while the matrix core already runs Q K^T of tile j+1; the
   // copies in flight during iteration j are K_{j+2} and V_{j+1}, so K_j and
   // V_j buffers alternate independently.
-  auto active = [&](int j) { return !CAUSAL || j * BN <= qw0 + 31; };
+  auto active = [&](int j) { return !CAUSAL || j * BN <= off + qw0 + 31; };
   issue_k(0, 0);
   issue_v(0, 0);
   if (n_kt > 1) issue_k(BN, 1);

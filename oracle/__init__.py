@@ -32,12 +32,12 @@ from .numerics import decode_bits, kv_bytes, kv_head_of
 from .attention import (one_shot, softmax_weights, tiled, splitk_merge, attention_rows)
 from .brute import brute_attention
 from .caches import ListCache, ContigCache, PagedCache
-from .decode import cached_decode, naive_decode, decode_step
+from .decode import cached_decode, naive_decode, decode_step, chunk_step
 
 __all__ = [
     "decode_bits", "kv_bytes", "kv_head_of",
     "one_shot", "softmax_weights", "tiled", "splitk_merge", "attention_rows",
     "brute_attention",
     "ListCache", "ContigCache", "PagedCache",
-    "cached_decode", "naive_decode", "decode_step",
+    "cached_decode", "naive_decode", "decode_step", "chunk_step",
 ]

@@ -14,10 +14,17 @@ Test infrastructure only (see the package docstring).
 * ``decode_step`` -- one batched decode step against a ``ContigCache`` or
   ``PagedCache``: append ``n_new`` tokens, then attend the single query of each
   head to ``lens[b] + n_new`` keys.
+* ``chunk_step`` -- a chunk of ``n_new`` new tokens per sequence with a query
+  each (prefix reuse, "KV缓存与Flash注意力" 实际应用 and 练习; a multi-token
+  append as in the cache class of "KV Cache:推理慢的真正原因", 缓存的是什么):
+  append the chunk, then query t of sequence b, which is token ``lens[b] + t``,
+  attends to keys ``0 .. lens[b] + t`` (causal) or to all ``lens[b] + n_new``.
 
 Pins: the two decoders agree bit for bit and produce 5050 vs 100 rows at
 n = 100 (tests/golden/op_counts.json); a decode step equals the matching row of
-causal prefill over the whole sequence (tests/test_oracle_decode.py).
+causal prefill over the whole sequence; a chunk step equals the matching rows
+of causal prefill over the whole sequence, reduces to a decode step at
+n_new = 1 and to plain prefill at an empty prefix (tests/test_oracle_decode.py).
 """
 from __future__ import annotations
 
@@ -106,4 +113,40 @@ def decode_step(cache, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
         o, ls = attention_rows(qb, K, V, scale, rows)
         for r, h in enumerate(hs):
             O[b, h], L[b, h] = o[r], ls[r]
+    return O, L
+
+
+def chunk_step(cache, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+               lens: np.ndarray, scale: float, dtype: str, causal: bool = True, rows=None):
+    """Append a chunk of ``n_new`` tokens per sequence, then attend its queries.
+
+    ``cache`` is a ``ContigCache`` or ``PagedCache`` (modified in place).
+    ``q`` [B, H_q, n_new, d] and the new rows [B, H_kv, n_new, d] are storage
+    bits; query t of sequence b is token ``lens[b] + t``.  ``rows`` optionally
+    restricts the output to a list of (b, h_q, t).  Returns (O, lse) in fp64:
+    [B, H_q, n_new, d] and [B, H_q, n_new] (rows not requested stay NaN).
+    """
+    cache.append(k_new, v_new, lens)
+    B, H_q, n_new, d = q.shape
+    O = np.full((B, H_q, n_new, d), np.nan)
+    L = np.full((B, H_q, n_new), np.nan)
+    wanted = rows if rows is not None else [(b, h, t) for b in range(B) for h in range(H_q)
+                                            for t in range(n_new)]
+    by_b = {}
+    for b, h, t in wanted:
+        by_b.setdefault(b, []).append((h, t))
+    for b, hts in sorted(by_b.items()):
+        n = int(lens[b]) + n_new
+        if isinstance(cache, PagedCache):
+            Kb, Vb = cache.gather(b, n)
+        else:
+            Kb, Vb = cache.view(b, n)
+        K = decode_bits(Kb, dtype)[None]
+        V = decode_bits(Vb, dtype)[None]
+        qb = decode_bits(q[b], dtype)[None]
+        # Nq = n_new queries against Nk = n keys: with the causal mask, query t
+        # sees keys j <= t + (n - n_new) = lens[b] + t
+        o, ls = attention_rows(qb, K, V, scale, [(0, h, t) for h, t in hts], causal=causal)
+        for r, (h, t) in enumerate(hts):
+            O[b, h, t], L[b, h, t] = o[r], ls[r]
     return O, L

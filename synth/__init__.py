@@ -152,6 +152,12 @@ DECODE_PAGED = DecodeCase("decode_bf16_gqa_paged_b64_hq32_hkv8", 64, 32, 8, 128,
 WORKLOADS = {c.name: c for c in (TINY_PREFILL, PREFILL_F16, PREFILL_BF16_CAUSAL,
                                  DECODE_CONTIG, DECODE_PAGED)}
 
+# Beyond the five: a chunked prefill against the paged cache, 512 new tokens per
+# sequence after a cached prefix of 0 .. 4096 tokens (shaped like the paged
+# decode layer: GQA 32 / 8 heads, d = 128).
+CHUNK_PAGED = DecodeCase("chunk_prefill_bf16_paged_b16_hq32_hkv8_n512", 16, 32, 8, 128, "bf16",
+                         0, 4096, True, 5, n_new=512)
+
 
 # --------------------------------------------------------------------------
 # prefill inputs
@@ -252,6 +258,30 @@ def decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
         out.update(k_pool=kp, v_pool=vp, block_table=table)
     del per_seq_k, per_seq_v
     return out
+
+
+def chunk_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Inputs of one chunked-prefill step: a chunk of ``case.n_new`` new tokens per
+    sequence, each with a query.
+
+    Everything of ``decode_inputs(case, lens)`` (cache before the chunk, lengths,
+    the chunk's K/V rows ``[B, H_kv, n_new, d]``); its single-token q is replaced
+    by the chunk's queries ``[B, H_q, n_new, d]`` drawn from ``SFC64(case.seed + 5000)``.
+    """
+    out = decode_inputs(case, lens=lens)
+    rng = make_rng(case.seed + 5000)
+    out["q"] = _normal(rng, (case.B, case.H_q, case.n_new, case.d), case.dtype)
+    return out
+
+
+def chunk_flops(lens: np.ndarray, n_new: int, H_q: int, d: int, causal: bool = True) -> float:
+    """Algorithmic FLOPs of a chunk step: 4*d per visible (query, key) pair."""
+    L = lens.astype(np.int64)
+    if causal:  # query t sees L + t + 1 keys
+        pairs = int(np.sum(L * n_new + n_new * (n_new + 1) // 2))
+    else:
+        pairs = int(np.sum((L + n_new) * n_new))
+    return 4.0 * d * H_q * pairs
 
 
 def tiny_decode_steps(case: PrefillCase = TINY_PREFILL, steps: int = TINY_DECODE_STEPS):

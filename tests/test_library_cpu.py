@@ -110,3 +110,24 @@ def test_append_rejects_bad_arguments():
     assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 0, 128, 64, 16, 0, 0, 2, None) == 1
     # contiguous with max_len 0
     assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 1, 128, 0, 16, 0, 0, 2, None) == 1
+
+
+@pytest.mark.parametrize("args,code", [
+    # (q, k_pool, v_pool, table, cache_lens, o, lse, B, H_q, H_kv, n_new, d, block_size,
+    #  max_blocks_per_seq, num_blocks, causal, scale, dtype)
+    ((0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 32, 128, 16, 8, 16, 1, 0.1, 2), 1),     # null q
+    ((FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, 2, 8, 2, 32, 128, 16, 8, 16, 1, 0.1, 2), 1),     # null table
+    ((FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, 2, 8, 2, 32, 128, 16, 8, 16, 1, 0.1, 2), 1),     # null lengths
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 6, 4, 32, 128, 16, 8, 16, 1, 0.1, 2), 1),  # H_q % H_kv
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 0, 128, 16, 8, 16, 1, 0.1, 2), 1),   # n_new = 0
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 200, 128, 16, 8, 16, 1, 0.1, 2), 1),  # n_new > 8 * 16
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 32, 128, 32, 8, 16, 1, 0.1, 2), 2),  # block size 32
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 32, 128, 16, 8, 16, 1, 0.1, 0), 2),  # f32
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 32, 32, 16, 8, 16, 1, 0.1, 2), 2),   # d = 32
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 32, 128, 16, 8, 16, 1, 0.0, 2), 2),  # scale 0
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, 0, 2, 8, 2, 32, 128, 16, 8, 16, 1, 0.1, 2), 1),  # misaligned o
+])
+def test_prefill_paged_rejects_bad_arguments(args, code):
+    L = _lib_or_skip()
+    assert L.attn_prefill_paged(*args, None) == code
+    assert L.attn_last_error()
