@@ -7,7 +7,10 @@ One step runs every stage of the path once, each on its own workload:
   * paged    : kv_append through a block table + attn_decode_paged, bf16, B=64,
                H_q=32, H_kv=8, d=128, cached lengths uniform in [128, 8192];
   * contig   : kv_append + attn_decode on a contiguous cache, bf16, B=32, H_q=64,
-               H_kv=8, d=128, cached lengths uniform in [1024, 32768].
+               H_kv=8, d=128, cached lengths uniform in [1024, 32768];
+  * chunk    : kv_append of 512 new tokens per sequence + attn_prefill_paged
+               (chunked prefill against the paged cache), bf16, B=16, H_q=32,
+               H_kv=8, d=128, cached prefixes uniform in [0, 4096].
 Inputs are seeded synthetic tensors already resident in HBM.  Each kernel call
 is bracketed by HIP events on the stream it runs on.
 
@@ -173,9 +176,22 @@ def main() -> int:
     c_lens_np = cinp["lens"]
     del cinp
     log(f"contiguous decode inputs ready ({time.perf_counter() - t_gen:.1f} s)")
+
+    # chunked prefill against a paged cache (beyond the five workloads)
+    kcase = synth.CHUNK_PAGED
+    kinp = synth.chunk_inputs(kcase)
+    kd = {n: to_dev(kinp[n], kcase.dtype, torch) for n in ("q", "k_new", "v_new", "k_pool", "v_pool")}
+    k_table = torch.from_numpy(kinp["block_table"]).cuda()
+    k_lens = torch.from_numpy(kinp["lens"]).cuda()
+    k_out = torch.empty_like(kd["q"])
+    k_lse = torch.empty(kd["q"].shape[:3], dtype=torch.float32, device="cuda")
+    k_flops = synth.chunk_flops(kinp["lens"], kcase.n_new, kcase.H_q, kcase.d, causal=True)
+    del kinp
+    log(f"chunk prefill inputs ready ({time.perf_counter() - t_gen:.1f} s)")
     torch.cuda.synchronize()
 
-    legs = ["prefill", "paged_append", "paged_decode", "contig_append", "contig_decode"]
+    legs = ["prefill", "paged_append", "paged_decode", "contig_append", "contig_decode", "chunk_append",
+            "chunk_prefill"]
 
     def step(ev=None):
         def rec(i):
@@ -194,6 +210,11 @@ def main() -> int:
         K.attn_decode(cdev["q"], cdev["k_cache"], cdev["v_cache"], c_seq, scale=ccase.sm_scale,
                       workspace=c_ws, out=c_out)
         rec(5)
+        K.kv_append(kd["k_pool"], kd["v_pool"], kd["k_new"], kd["v_new"], k_lens, k_table)
+        rec(6)
+        K.attn_prefill_paged(kd["q"], kd["k_pool"], kd["v_pool"], k_table, k_lens, causal=True,
+                             scale=kcase.sm_scale, return_lse=True, out=k_out, lse=k_lse)
+        rec(7)
 
     if args.calibrate_copy:
         # torch's elementwise multiply: reads 2^30 bytes, writes 2^30 bytes per launch
@@ -207,7 +228,7 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(legs) + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -231,6 +252,7 @@ def main() -> int:
     pf_tflops = pf_flops / (ms["prefill"] * 1e-3) / 1e12
     g_gbs = g_bytes / (ms["paged_decode"] * 1e-3) / 1e9
     c_gbs = c_bytes / (ms["contig_decode"] * 1e-3) / 1e9
+    k_tflops = k_flops / (ms["chunk_prefill"] * 1e-3) / 1e12
 
     def roof(bound, achieved, peak, unit, kernel, per_unit):
         return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -267,6 +289,13 @@ def main() -> int:
             "append_ms": round(ms["contig_append"], 4),
             "roofline": roof("hbm", c_gbs, PEAK_HBM_GBS, "GB/s", "decode_mfma_kernel<BF16,128,contig>+merge",
                              {"bytes": c_bytes}),
+        },
+        "chunk_prefill_paged": {
+            "value": round(k_tflops, 2), "unit": "TFLOP/s", "workload": kcase.name,
+            "flops": k_flops, "ms_mean": round(ms["chunk_prefill"], 4), "ms_median": round(med["chunk_prefill"], 4),
+            "append_ms": round(ms["chunk_append"], 4),
+            "roofline": roof("mfma", k_tflops, PEAK_BF16_TFLOPS, "TFLOP/s",
+                             "prefill_mfma_kernel<BF16,128,causal,paged>", {"flops": k_flops}),
         },
         "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
         "device_error_flags": flags,

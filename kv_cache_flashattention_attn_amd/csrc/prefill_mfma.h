@@ -115,6 +115,31 @@ __device__ __forceinline__ void prefill_block_order(int bid, int n_qt, int total
   qt = causal ? n_qt - 1 - bid % n_qt : bid % n_qt;
 }
 
+// Workgroup order for chunked prefill.  The work of a sequence grows with its
+// cached prefix, so sequences run longest prefix first: KV heads are listed
+// sequence by sequence in that order and dealt to the XCDs round-robin, which
+// also spreads every sequence over all XCDs.  The G query heads and the query
+// blocks of one KV head run next to each other, so they find its K/V in the
+// XCD's L2.  rank_to_seq(r) returns the sequence of rank r.
+template <typename RankToSeq>
+__device__ __forceinline__ void chunk_block_order(int bid, int n_qt, int H_q, int H_kv, int KV, bool causal,
+                                                  RankToSeq rank_to_seq, int& bh, int& qt) {
+  const int G = H_q / H_kv, per_kv = G * n_qt;
+  int pos, rr;
+  if (KV % kNumXcd == 0) {
+    const int x = bid % kNumXcd, k = bid / kNumXcd;
+    pos = (k / per_kv) * kNumXcd + x;
+    rr = k % per_kv;
+  } else {
+    pos = bid / per_kv;
+    rr = bid % per_kv;
+  }
+  const int b = rank_to_seq(pos / H_kv), g = pos % H_kv;
+  const int hq = rr / n_qt, qi = rr % n_qt;
+  bh = b * H_q + g * G + hq;
+  qt = causal ? n_qt - 1 - qi : qi;
+}
+
 // Keys and values of a paged cache (chunked prefill): pools
 // [num_blocks, H_kv, 16, d], token p of sequence b in block
 // table[b * max_blocks_per_seq + p / 16], row p % 16; the N queries of
@@ -124,6 +149,9 @@ struct PagedKV {
   int max_blocks_per_seq;
   int num_blocks;
 };
+// Block ids a workgroup keeps in LDS (32K tokens); ids past them are read
+// from the table directly.
+constexpr int kLdsBlocks = 2048;
 
 template <typename T, int D, int NW, bool CAUSAL, bool LSE, bool PAGED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
@@ -137,6 +165,8 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
 
   // [buffer][K, V] tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][TILE];
+  // paged: the sequence's (validated) block ids
+  __shared__ __attribute__((aligned(16))) int32_t blk_lds[PAGED ? kLdsBlocks : 1];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -145,7 +175,27 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
   const int n_qt = (a.N + BM - 1) / BM;
   const int total = n_qt * BH;
   int bh, qt;
-  prefill_block_order(blockIdx.x, n_qt, total, CAUSAL, bh, qt);
+  if (PAGED) {
+    // rank of sequence i = sequences with a longer prefix, or an equal one and
+    // a smaller index; lane i of each 64-sequence slice ranks sequence i
+    auto rank_to_seq = [&](int r) {
+      for (int s0 = 0; s0 < a.B; s0 += 64) {
+        const int i = s0 + (tid & 63);
+        const int li = i < a.B ? cache_lens[i] : 0;
+        int rank = 0;
+        for (int jj = 0; jj < a.B; ++jj) {
+          const int lj = cache_lens[jj];
+          rank += (lj > li || (lj == li && jj < i)) ? 1 : 0;
+        }
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(i < a.B && rank == r);
+        if (hit != 0) return s0 + (int)__builtin_ctzll(hit);
+      }
+      return 0;  // not reached: ranks are a permutation of 0 .. B-1
+    };
+    chunk_block_order(blockIdx.x, n_qt, a.H_q, a.H_kv, a.B * a.H_kv, CAUSAL, rank_to_seq, bh, qt);
+  } else {
+    prefill_block_order(blockIdx.x, n_qt, total, CAUSAL, bh, qt);
+  }
   const int b = bh / a.H_q, h = bh % a.H_q;
   const int g = h / (a.H_q / a.H_kv);
   const int q0 = qt * BM;
@@ -186,30 +236,59 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
   // one tensor's tile: src = K or V, off = its lane offset, which = 0 (K) / 1 (V)
   // paged: the chunk offset of this lane's 16 bytes within its row
   const uint32_t kch = 16 * ((l % CH) ^ Gm::swz_k(r0)), vch = 16 * ((l % CH) ^ Gm::swz_v(r0));
-  // block id of key position p (an id outside the pool reads block 0 and raises a flag)
-  auto block_at = [&](int p) {
-    int blk = table[(size_t)b * pk.max_blocks_per_seq + (p >> 4)];
+  // block id of the table slot j (an id outside the pool reads block 0 and raises a flag)
+  auto checked_block = [&](int j) {
+    int blk = table[(size_t)b * pk.max_blocks_per_seq + j];
     if (blk < 0 || blk >= pk.num_blocks) {
-      if (l == 0) raise_device_error(2);
+      raise_device_error(2);
       blk = 0;
     }
     return blk;
+  };
+  // block id of key position p: from LDS (filled below, before the first copy)
+  auto block_at = [&](int p) {
+    const int j = p >> 4;
+    const int blk = j < kLdsBlocks ? __builtin_amdgcn_readfirstlane(blk_lds[j]) : checked_block(j);
+    return min(max(blk, 0), pk.num_blocks - 1);  // already valid; kept inside the pool regardless
   };
   auto issue_paged = [&](const uint16_t* src, const uint32_t ch, int which, int k0, int buf) {
     const uint32_t dst = smem_base + (2 * buf + which) * TILE + w * 1024;
     const uint8_t* base = reinterpret_cast<const uint8_t*>(src);
     const int last = Nk - 1;
-    const int blk_last = block_at(last);
+    // the tile's 4 block ids with one LDS read (slot k0 / 16 is a multiple of 4)
+    const int j0 = k0 >> 4;
+    int ids[4];
+    if (j0 + 3 < kLdsBlocks) {
+      const int4 v4 = *reinterpret_cast<const int4*>(&blk_lds[j0]);
+      ids[0] = __builtin_amdgcn_readfirstlane(v4.x);
+      ids[1] = __builtin_amdgcn_readfirstlane(v4.y);
+      ids[2] = __builtin_amdgcn_readfirstlane(v4.z);
+      ids[3] = __builtin_amdgcn_readfirstlane(v4.w);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ids[u] = (j0 + u) * 16 <= last ? checked_block(j0 + u) : 0;
+    }
+    const bool ragged = k0 + BN > Nk;
+    // rows past the last key read the last key instead (ragged last tile only)
+    const int blk_last = ragged ? min(max(block_at(last), 0), pk.num_blocks - 1) : 0;
+    const uint32_t lane_off = (l / CH) * ROWB + ch;  // this lane's bytes within the copy's rows
 #pragma unroll
     for (int i = 0; i < Gm::COPIES; ++i) {
-      // the copy's ROWS_PER_COPY rows lie in one 16-row block; rows past the
-      // last key read the last key instead
+      // the copy's ROWS_PER_COPY rows lie in one 16-row block of the tile
       const int fr = k0 + w * Gm::ROWS_PER_COPY + i * NW * Gm::ROWS_PER_COPY;
-      const int blk = fr <= last ? block_at(fr) : blk_last;
-      const int r = fr + l / CH;
-      const bool in = r <= last;
-      const size_t row = ((size_t)(in ? blk : blk_last) * a.H_kv + g) * 16 + ((in ? r : last) & 15);
-      lds_copy16(base + row * ROWB + ch, dst + i * kCopyStride);
+      const int slot = (fr >> 4) - j0;  // 0 .. 3, wave-uniform
+      int blk = slot == 0 ? ids[0] : slot == 1 ? ids[1] : slot == 2 ? ids[2] : ids[3];
+      blk = min(max(blk, 0), pk.num_blocks - 1);  // valid already; kept inside the pool regardless
+      if (!ragged) {
+        // wave-uniform row base (scalar registers) plus one lane offset
+        const uint8_t* cb = base + (((size_t)blk * a.H_kv + g) * 16 + (fr & 15)) * ROWB;
+        lds_copy16(cb, lane_off, dst + i * kCopyStride);
+      } else {
+        const int r = fr + l / CH;
+        const bool in = r <= last;
+        const size_t row = ((size_t)(in ? blk : blk_last) * a.H_kv + g) * 16 + ((in ? r : last) & 15);
+        lds_copy16(base + row * ROWB + ch, dst + i * kCopyStride);
+      }
     }
   };
   auto issue = [&](const uint16_t* src, const uint32_t off, int which, int k0, int buf) {
@@ -361,6 +440,13 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
   // copies in flight during iteration j are K_{j+2} and V_{j+1}, so K_j and
   // V_j buffers alternate independently.
   auto active = [&](int j) { return !CAUSAL || j * BN <= off + qw0 + 31; };
+  if (PAGED) {
+    // every block the copies can touch: the tiles reach past key_end, and
+    // rows past the last key read the last key (block of Nk - 1)
+    const int nb = min((Nk + 15) >> 4, kLdsBlocks);
+    for (int j = tid; j < nb; j += 64 * NW) blk_lds[j] = checked_block(j);
+    __syncthreads();
+  }
   issue_k(0, 0);
   issue_v(0, 0);
   if (n_kt > 1) issue_k(BN, 1);
