@@ -179,13 +179,18 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
     // rank of sequence i = sequences with a longer prefix, or an equal one and
     // a smaller index; lane i of each 64-sequence slice ranks sequence i
     auto rank_to_seq = [&](int r) {
+      const int lane = tid & 63;
       for (int s0 = 0; s0 < a.B; s0 += 64) {
-        const int i = s0 + (tid & 63);
+        const int i = s0 + lane;
         const int li = i < a.B ? cache_lens[i] : 0;
         int rank = 0;
-        for (int jj = 0; jj < a.B; ++jj) {
-          const int lj = cache_lens[jj];
-          rank += (lj > li || (lj == li && jj < i)) ? 1 : 0;
+        for (int t0 = 0; t0 < a.B; t0 += 64) {  // other lengths, 64 per vector load, shared by readlane
+          const int lt = t0 + lane < a.B ? cache_lens[t0 + lane] : 0;
+          const int nt = min(64, a.B - t0);
+          for (int u = 0; u < nt; ++u) {
+            const int lj = __builtin_amdgcn_readlane(lt, u);
+            rank += (lj > li || (lj == li && t0 + u < i)) ? 1 : 0;
+          }
         }
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(i < a.B && rank == r);
         if (hit != 0) return s0 + (int)__builtin_ctzll(hit);
