@@ -188,6 +188,42 @@ int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
                        int max_blocks_per_seq, int num_blocks, int causal, float scale,
                        int dtype, void* stream);
 
+/*
+ * kv_append_fp8 / attn_decode_paged_fp8 -- a paged KV cache stored in 8 bits.
+ *
+ * Storing the cache in 8 bits halves the bytes decode must read ("KV Cache:
+ * 推理慢的真正原因", 工程优化手段 / quantization; the fp8 KV-cache option listed
+ * in "KV缓存与Flash注意力", 实际应用).  Format: OCP FP8 E4M3 (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, no infinities, largest finite 448), one
+ * per-tensor scale for K and one for V:
+ *   stored = E4M3(x * (1 / k_scale))   -- x converted exactly to fp32, the product
+ *            rounded to the nearest E4M3 value, ties to even, saturating at
+ *            +-448; NaN stays NaN.  1 / k_scale is computed in fp32.
+ *   value  = E4M3 value * k_scale      (likewise for V with v_scale)
+ * The pools are [num_blocks, H_kv, 16, d] bytes; block table and lengths as for
+ * kv_append / attn_decode_paged.
+ */
+/* Append n_new tokens' K/V ([B, H_kv, n_new, d] in `dtype`: F32, F16 or BF16),
+ * quantized, at positions cache_lens[b] ..; cache_lens is not advanced.
+ * Errors: INVALID_ARG (pointers, sizes, scales <= 0 or not finite),
+ *         UNSUPPORTED (dtype, d, block_size != 16), HIP. */
+int kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                  const int32_t* cache_lens, const int32_t* block_table,
+                  int B, int H_kv, int n_new, int d, int block_size,
+                  int max_blocks_per_seq, int num_blocks, int dtype,
+                  float k_scale, float v_scale, void* stream);
+
+/* attn_decode_paged over the FP8 pools: q, o [B, H_q, d] in `dtype` (F16 or
+ * BF16), d = 64 or 128, scale > 0.  Same workspace as attn_decode_paged.
+ * Errors: as attn_decode_paged; UNSUPPORTED for other dtypes / d. */
+int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          void* o, float* lse,
+                          int B, int H_q, int H_kv, int d, int block_size,
+                          int max_blocks_per_seq, int num_blocks, float scale,
+                          float k_scale, float v_scale, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes attn_decode / attn_decode_paged need for a cache capacity of
  * max_seq_len tokens per sequence.  0 on invalid sizes. */
 size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d);

@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "AttnError", "lib", "lib_path", "attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode",
-    "attn_decode_paged",
+    "attn_decode_paged", "kv_append_fp8", "attn_decode_paged_fp8",
     "attn_decode_workspace_bytes", "attn_device_error_flags", "attn_version", "DTYPE_CODES",
     "EXPORTED_SYMBOLS",
 ]
@@ -35,6 +35,7 @@ DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16:
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
           4: "ATTN_ERR_HIP"}
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
+                    "kv_append_fp8", "attn_decode_paged_fp8",
                     "attn_decode_workspace_bytes", "attn_last_error", "attn_version",
                     "attn_device_error_flags")
 
@@ -62,6 +63,9 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                      i32, vp]
     L.kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp]
+    L.kv_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+    L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32,
+                                        f32, i32, vp, sz, vp]
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                     vp, sz, vp]
@@ -71,7 +75,7 @@ def lib() -> ctypes.CDLL:
     L.attn_version.restype = ctypes.c_char_p
     L.attn_device_error_flags.argtypes = [vp]
     for name in ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
-                 "attn_device_error_flags"):
+                 "kv_append_fp8", "attn_decode_paged_fp8", "attn_device_error_flags"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -230,6 +234,48 @@ def attn_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
                                  _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                  _stream())
     _check("attn_decode_paged", rc)
+    return (out, lse) if return_lse else out
+
+
+def kv_append_fp8(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                  cache_lens: torch.Tensor, block_table: torch.Tensor, k_scale: float = 1.0,
+                  v_scale: float = 1.0) -> None:
+    """Quantize and append k_new, v_new [B, H_kv, n_new, d] into FP8 E4M3 pools (uint8
+    tensors [num_blocks, H_kv, 16, d])."""
+    B, H_kv, n_new, d = k_new.shape
+    nb, _, bs, _ = k_pool.shape
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise ValueError("FP8 pools are uint8 tensors of E4M3 codes")
+    rc = lib().kv_append_fp8(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                             _dev(v_new, "v_new"), _dev(cache_lens, "cache_lens", torch.int32),
+                             _dev(block_table, "block_table", torch.int32), B, H_kv, n_new, d, bs,
+                             block_table.shape[1], nb, _code(k_new), float(k_scale), float(v_scale), _stream())
+    _check("kv_append_fp8", rc)
+
+
+def attn_decode_paged_fp8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
+                          scale: Optional[float] = None, return_lse: bool = False,
+                          workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None):
+    """attn_decode_paged over FP8 E4M3 pools (uint8 [num_blocks, H_kv, 16, d])."""
+    B, H_q, d = q.shape
+    nb, H_kv, bs, _ = k_pool.shape
+    mbps = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = attn_decode_workspace_bytes(B, H_q, mbps * bs, d)
+    workspace = _workspace(workspace, nbytes, q.device)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    rc = lib().attn_decode_paged_fp8(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                     _dev(block_table, "block_table", torch.int32),
+                                     _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
+                                     _dev(lse, "lse", torch.float32) if return_lse else 0,
+                                     B, H_q, H_kv, d, bs, mbps, nb, scale, float(k_scale), float(v_scale), _code(q),
+                                     _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                     _stream())
+    _check("attn_decode_paged_fp8", rc)
     return (out, lse) if return_lse else out
 
 

@@ -163,16 +163,16 @@ int launch_decode_plain(const attn::DecodeArgs& a, hipStream_t st) {
   return launch_status("attn_decode");
 }
 
-template <typename T, int D, bool PAGED>
-int launch_decode_mfma(const attn::DecodeArgs& a, int32_t* piece_cnt, hipStream_t st) {
+template <typename T, int D, bool PAGED, bool FP8>
+int launch_decode_mfma(const attn::DecodeArgs& a, int32_t* piece_cnt, hipStream_t st, float v_scale = 1.f) {
   const int G = a.H_q / a.H_kv;
-  const attn::DecodeStreamArgs sa{a, piece_cnt, (G + 15) / 16};
-  const void* kernel = reinterpret_cast<const void*>(&attn::decode_mfma_kernel<T, D, PAGED>);
+  const attn::DecodeStreamArgs sa{a, piece_cnt, (G + 15) / 16, v_scale};
+  const void* kernel = reinterpret_cast<const void*>(&attn::decode_mfma_kernel<T, D, PAGED, FP8>);
   static int grid = 0;  // one value per instantiation; every device here is an MI355X
   if (grid == 0) grid = resident_grid(kernel, 64 * attn::kDecWaves);
   if (grid <= 0) return fail(ATTN_ERR_HIP, "attn_decode: occupancy query failed");
-  hipLaunchKernelGGL((attn::decode_mfma_kernel<T, D, PAGED>), dim3(grid), dim3(64 * attn::kDecWaves), 0, st, sa,
-                     a.seq_lens, a.table);
+  hipLaunchKernelGGL((attn::decode_mfma_kernel<T, D, PAGED, FP8>), dim3(grid), dim3(64 * attn::kDecWaves), 0, st,
+                     sa, a.seq_lens, a.table);
   return launch_status("attn_decode");
 }
 
@@ -190,7 +190,7 @@ template <typename T, int D, bool PAGED>
 int decode_typed(const attn::DecodeArgs& a, void* o, float* lse, bool mfma, int32_t* piece_cnt, hipStream_t st) {
   if constexpr ((D == 64 || D == 128) && !std::is_same<T, attn::F32>::value) {
     if (mfma) {
-      const int rc = launch_decode_mfma<T, D, PAGED>(a, piece_cnt, st);
+      const int rc = launch_decode_mfma<T, D, PAGED, false>(a, piece_cnt, st);
       if (rc != ATTN_OK) return rc;
       return launch_merge<T, D>(a, o, lse, 0, piece_cnt, st);
     }
@@ -222,6 +222,16 @@ int decode_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, int d
     case ATTN_BF16: return decode_d<attn::BF16, PAGED>(a, o, lse, d, mfma, cnt, st);
   }
   return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: dtype %d not supported", dtype);
+}
+
+// FP8 paged cache: the MFMA decode reading E4M3 K/V, then the merge.
+template <typename T>
+int decode_fp8_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, float v_scale, int32_t* cnt,
+                        hipStream_t st) {
+  int rc = d == 64 ? launch_decode_mfma<T, 64, true, true>(a, cnt, st, v_scale)
+                   : launch_decode_mfma<T, 128, true, true>(a, cnt, st, v_scale);
+  if (rc != ATTN_OK) return rc;
+  return d == 64 ? launch_merge<T, 64>(a, o, lse, 0, cnt, st) : launch_merge<T, 128>(a, o, lse, 0, cnt, st);
 }
 
 int check_decode_common(const char* fn, const void* q, const void* k, const void* v, const int32_t* lens,
@@ -355,9 +365,17 @@ size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d) {
 static int decode_common(const char* fn, bool paged, const void* q, const void* k, const void* v,
                          const int32_t* table, const int32_t* seq_lens, void* o, float* lse, int B, int H_q,
                          int H_kv, int capacity, int mbps, int num_blocks, int d, float scale, int dtype,
-                         void* workspace, size_t workspace_bytes_given, void* stream) {
+                         void* workspace, size_t workspace_bytes_given, void* stream, bool fp8 = false,
+                         float k_scale = 1.f, float v_scale = 1.f) {
   int rc = check_decode_common(fn, q, k, v, seq_lens, o, B, H_q, H_kv, d, dtype, scale);
   if (rc != ATTN_OK) return rc;
+  if (fp8) {
+    if (!(dtype == ATTN_F16 || dtype == ATTN_BF16) || !(d == 64 || d == 128))
+      return fail(ATTN_ERR_UNSUPPORTED, "%s: f16/bf16 queries with d = 64 or 128 only", fn);
+    if (!(scale > 0.f)) return fail(ATTN_ERR_UNSUPPORTED, "%s: scale must be positive", fn);
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+      return fail(ATTN_ERR_INVALID_ARG, "%s: k_scale and v_scale must be finite and positive", fn);
+  }
   if (capacity < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: cache capacity must be >= 1", fn);
   const size_t need = workspace_bytes(B, H_q, capacity, d);
   if (!workspace || workspace_bytes_given < need)
@@ -381,9 +399,12 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
   a.max_blocks_per_seq = mbps;
   a.num_blocks = num_blocks;
   a.s_max = S;
-  a.scale_log2 = scale * attn::kLog2e;
+  a.scale_log2 = scale * (fp8 ? k_scale : 1.f) * attn::kLog2e;
   int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.cnt_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fp8)
+    return dtype == ATTN_BF16 ? decode_fp8_dispatch<attn::BF16>(a, o, lse, d, v_scale, cnt, st)
+                              : decode_fp8_dispatch<attn::F16>(a, o, lse, d, v_scale, cnt, st);
   return paged ? decode_dispatch<true>(a, o, lse, d, dtype, scale, cnt, st)
                : decode_dispatch<false>(a, o, lse, d, dtype, scale, cnt, st);
 }
@@ -409,6 +430,52 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, con
   return decode_common("attn_decode_paged", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q, H_kv,
                        max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
                        workspace_bytes_given, stream);
+}
+
+int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d,
+                          int block_size, int max_blocks_per_seq, int num_blocks, float scale, float k_scale,
+                          float v_scale, int dtype, void* workspace, size_t workspace_bytes_given, void* stream) {
+  if (!block_table) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_fp8: null block table");
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_fp8: block_size must be 16 (got %d)", block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_fp8: max_blocks_per_seq and num_blocks must be >= 1");
+  if ((long long)max_blocks_per_seq * 16 > 0x7FFFFFFFLL)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_fp8: max_blocks_per_seq too large");
+  return decode_common("attn_decode_paged_fp8", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q,
+                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
+                       workspace_bytes_given, stream, true, k_scale, v_scale);
+}
+
+int kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* cache_lens,
+                  const int32_t* block_table, int B, int H_kv, int n_new, int d, int block_size,
+                  int max_blocks_per_seq, int num_blocks, int dtype, float k_scale, float v_scale, void* stream) {
+  if (!k_pool || !v_pool || !k_new || !v_new || !cache_lens || !block_table)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: null pointer");
+  if (B < 1 || H_kv < 1 || n_new < 1) return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: B, H_kv, n_new must be >= 1");
+  if (!valid_dtype(dtype)) return fail(ATTN_ERR_UNSUPPORTED, "kv_append_fp8: dtype %d not supported", dtype);
+  if (!plain_head_dim(d)) return fail(ATTN_ERR_UNSUPPORTED, "kv_append_fp8: head dim %d not supported", d);
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "kv_append_fp8: block_size must be 16 (got %d)", block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: max_blocks_per_seq and num_blocks must be >= 1");
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: k_scale and v_scale must be finite and positive");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: tensors must be 16-byte aligned");
+  attn::AppendFp8Args a{static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_new, v_new, cache_lens,
+                        block_table, B, H_kv, n_new, d, max_blocks_per_seq, num_blocks, 1.0f / k_scale,
+                        1.0f / v_scale};
+  const long long threads = (long long)B * H_kv * n_new * (d / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case ATTN_F32: hipLaunchKernelGGL(attn::kv_append_fp8_kernel<attn::F32>, grid, dim3(256), 0, st, a); break;
+    case ATTN_F16: hipLaunchKernelGGL(attn::kv_append_fp8_kernel<attn::F16>, grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(attn::kv_append_fp8_kernel<attn::BF16>, grid, dim3(256), 0, st, a); break;
+  }
+  return launch_status("kv_append_fp8");
 }
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }

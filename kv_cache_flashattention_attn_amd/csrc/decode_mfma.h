@@ -32,6 +32,7 @@
 // segment belongs to the p-th wave whose share overlaps it);
 // decode_merge_kernel combines the pieces with their log-sum-exp weights.
 #pragma once
+#include <type_traits>
 #include "decode_plain.h"
 #include "mfma_common.h"
 
@@ -88,6 +89,7 @@ struct DecodeStreamArgs {
   DecodeArgs a;
   int32_t* piece_cnt;  // [B][H_q]: pieces of segment (b, gh), written by the wave holding piece 0
   int n_hg;            // groups of 16 query heads per KV head
+  float v_scale;       // fp8 cache: V = stored value * v_scale (1 otherwise)
 };
 
 // Sum over the wave (uniform result).
@@ -101,13 +103,32 @@ __device__ __forceinline__ int wave_sum(int x) {
 // nothing the kernel writes aliases them, so the compiler can read them with
 // scalar loads inside the stage loop (vector loads there would count against
 // the vmcnt waits of the stage copies).
-template <typename T, int D, bool PAGED>
+// Two FP8 E4M3 values (byte pair `hi` of word x) -> two 16-bit T values.  Every
+// E4M3 value is exact in bf16 and f16, so this is a pure format change.
+template <typename T, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to(uint32_t x) {
+  if constexpr (std::is_same<T, BF16>::value)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
+}
+// 16 bytes of FP8 (words w[0..3]) -> 16 values of T in two 16-byte vectors
+template <typename T>
+__device__ __forceinline__ void fp8x16_to(const u32x4 w, u32x4& lo, u32x4& hi) {
+  lo = u32x4{fp8x2_to<T, false>(w[0]), fp8x2_to<T, true>(w[0]), fp8x2_to<T, false>(w[1]), fp8x2_to<T, true>(w[1])};
+  hi = u32x4{fp8x2_to<T, false>(w[2]), fp8x2_to<T, true>(w[2]), fp8x2_to<T, false>(w[3]), fp8x2_to<T, true>(w[3])};
+}
+
+template <typename T, int D, bool PAGED, bool FP8>
 __global__ void __launch_bounds__(64 * kDecWaves)
 decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const int32_t* __restrict__ table) {
   using Gm = DecGeom<D>;
   constexpr int KS = D / 32;   // 32-deep k-steps of Q K^T
   constexpr int DB = D / 16;   // 16-wide blocks of d
   constexpr int ROWB = Gm::ROWB, VCH = Gm::VCH;
+  // bytes per cache row, and 16-byte pieces of K and of V a lane loads per stage
+  constexpr int RB = FP8 ? D : ROWB;
+  constexpr int NKL = FP8 ? D / 64 : KS, NVL = FP8 ? D / 64 : VCH;
 
   __shared__ __attribute__((aligned(1024))) uint8_t vtile[kDecWaves * Gm::SLOT];
 
@@ -204,8 +225,8 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // 64 bytes at byte 64 (l % 4)), and the query fragments when the stage
   // starts a segment.
   struct Stage {
-    u32x4 k[KS];
-    u32x4 v[VCH];
+    u32x4 k[NKL];
+    u32x4 v[NVL];
     u32x4 q[KS];
     bool ok;     // valid block id (paged)
     bool qnew;   // q holds a new segment's query rows
@@ -231,19 +252,32 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     // contiguous: rows past the capacity (last stage only) read the last row instead
     const int kr = PAGED ? col : min(col, a.capacity - 1 - c.st * kDecStage);
     const int vr = PAGED ? (l >> 2) : min(l >> 2, a.capacity - 1 - c.st * kDecStage);
-    const uint8_t* ks_src = kp + (row0 + kr) * ROWB + 16 * grp;
+    if (FP8) {
+      // FP8 rows: lane (col, grp) takes the d-chunks KS grp .. KS grp + KS - 1 of
+      // its key row (8 KS contiguous bytes); the query fragments use the same
+      // assignment of d to k-steps, so the dot products are unchanged.  V: the
+      // same rows and columns as the 16-bit layout, a quarter row per lane.
+      const uint8_t* ks_src = kp + (row0 + kr) * RB + 8 * KS * grp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) S.k[ks] = *reinterpret_cast<const u32x4*>(ks_src + 64 * ks);
-    const uint8_t* vs_src = vp + (row0 + vr) * ROWB + (ROWB / 4) * (l & 3);
+      for (int i = 0; i < NKL; ++i) S.k[i] = *reinterpret_cast<const u32x4*>(ks_src + 16 * i);
+      const uint8_t* vs_src = vp + (row0 + vr) * RB + (RB / 4) * (l & 3);
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) S.v[i] = *reinterpret_cast<const u32x4*>(vs_src + 16 * i);
+      for (int i = 0; i < NVL; ++i) S.v[i] = *reinterpret_cast<const u32x4*>(vs_src + 16 * i);
+    } else {
+      const uint8_t* ks_src = kp + (row0 + kr) * ROWB + 16 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) S.k[ks] = *reinterpret_cast<const u32x4*>(ks_src + 64 * ks);
+      const uint8_t* vs_src = vp + (row0 + vr) * ROWB + (ROWB / 4) * (l & 3);
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) S.v[i] = *reinterpret_cast<const u32x4*>(vs_src + 16 * i);
+    }
     S.qnew = seg_start(c);
     if (S.qnew) {
       // query heads g*G + 16 hg + col (columns past the group repeat head g*G)
       const int gi = 16 * hg + col;
-      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * D + 8 * grp;
+      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * D + (FP8 ? 8 * KS : 8) * grp;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + (FP8 ? 8 : 32) * ks);
     }
   };
 
@@ -269,7 +303,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = oacc[db] * inv;
+        *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = oacc[db] * (FP8 ? inv * sa.v_scale : inv);
       if (grp == 0) a.part_lse[pidx] = e_tot > 0.f ? (m + __log2f(e_tot)) * kLn2 : kNegInf;
     }
   };
@@ -290,18 +324,37 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       if (piece == 0 && l == 0)
         sa.piece_cnt[(size_t)c.b * a.H_q + c.gh] = (seg0 + c.n - 1) / share - seg0 / share + 1;
     }
-    // V rows into the LDS tile (row l / 4, logical chunks VCH (l % 4) + i)
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
+    // V rows into the LDS tile (row l / 4, logical chunks VCH (l % 4) + i), and
+    // S^T = K Q^T: lane holds head col, tokens t0 + 4 grp + i.  An FP8 stage is
+    // first widened to 16-bit values.
+    auto put_v = [&](const int i, const u32x4 x) {
       const int r = l >> 2;
       const int ch = (VCH * (l & 3) + i) ^ Gm::swz_v(r);
-      *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ch) = S.v[i];
-    }
-    // S^T = K Q^T: lane holds head col, tokens t0 + 4 grp + i
+      *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ch) = x;
+    };
     const int t0 = c.st * kDecStage;
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP8) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sacc = mfma16k32<T>(S.k[ks], qf[ks], sacc);
+      for (int i = 0; i < NVL; ++i) {
+        u32x4 lo, hi;
+        fp8x16_to<T>(S.v[i], lo, hi);
+        put_v(2 * i, lo);
+        put_v(2 * i + 1, hi);
+      }
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) {
+        u32x4 lo, hi;
+        fp8x16_to<T>(S.k[i], lo, hi);
+        sacc = mfma16k32<T>(lo, qf[2 * i], sacc);
+        sacc = mfma16k32<T>(hi, qf[2 * i + 1], sacc);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) put_v(i, S.v[i]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc = mfma16k32<T>(S.k[ks], qf[ks], sacc);
+    }
     if (!S.ok || t0 + kDecStage > c.len) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)

@@ -74,4 +74,96 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
   a.v_cache[dst] = vv;
 }
 
+// ---------------------------------------------------------------------------
+// FP8 cache: append with quantization.
+//
+// The pages name an 8-bit KV cache as a way to halve its bytes ("KV Cache:推理慢的
+// 真正原因", 工程优化手段 / quantization; the fp8 KV-cache option in
+// "KV缓存与Flash注意力", 实际应用).  Stored value = E4M3(x * inv_scale): x is
+// the input converted exactly to fp32, inv_scale = 1 / scale in fp32, and the
+// product is rounded to the nearest OCP FP8 E4M3 value (ties to even),
+// saturating at +-448; NaN stays NaN.  Dequantized value = E4M3 value * scale.
+
+// fp32 -> OCP FP8 E4M3 code (round to nearest even, saturating)
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return s | 0x7Fu;        // NaN
+  if (a >= 448.f) return s | 0x7Eu;    // saturate (448 = 1.75 * 2^8 is the largest finite value)
+  if (a < 0.015625f) {                 // below 2^-6: subnormal grid of 2^-9
+    return s | (uint32_t)__builtin_rintf(a * 512.f);  // 0 .. 8; 8 is the smallest normal
+  }
+  // normal: keep 3 mantissa bits, rounding the 20 dropped bits to nearest even
+  const uint32_t ua = __float_as_uint(a);
+  const uint32_t r = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) & 0xFFF00000u;
+  const int e = (int)(r >> 23) - 127;  // -6 .. 8 (a < 448 cannot round past 448)
+  return s | (uint32_t)((e + 7) << 3) | ((r >> 20) & 7u);
+}
+
+template <typename TIN>
+__device__ __forceinline__ float in_to_f32(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ float in_to_f32<F32>(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+template <>
+__device__ __forceinline__ float in_to_f32<BF16>(const void* p, int64_t i) {
+  return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
+}
+template <>
+__device__ __forceinline__ float in_to_f32<F16>(const void* p, int64_t i) {
+  return (float)static_cast<const _Float16*>(p)[i];
+}
+
+struct AppendFp8Args {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* cache_lens;
+  const int32_t* block_table;
+  int B, H_kv, n_new, d;
+  int max_blocks_per_seq, num_blocks;
+  float k_inv, v_inv;  // 1 / scale, in fp32
+};
+
+// One thread quantizes 8 consecutive elements of a K row and of the V row.
+template <typename TIN>
+__global__ void __launch_bounds__(256) kv_append_fp8_kernel(AppendFp8Args a) {
+  const int per_row = a.d / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.H_kv * a.n_new * per_row;
+  if (idx >= total) return;
+  const int c = (int)(idx % per_row);
+  const int64_t row = idx / per_row;  // ((b*H_kv)+h)*n_new+t
+  const int t = (int)(row % a.n_new);
+  const int h = (int)((row / a.n_new) % a.H_kv);
+  const int b = (int)(row / ((int64_t)a.n_new * a.H_kv));
+  const int start = a.cache_lens[b];
+  if (start < 0) {
+    if (c == 0) raise_device_error(4);
+    return;
+  }
+  const int64_t p = (int64_t)start + t;
+  const int64_t lb = p >> 4;
+  if (lb >= a.max_blocks_per_seq) {
+    if (c == 0) raise_device_error(1);
+    return;
+  }
+  const int blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + lb];
+  if (blk < 0 || blk >= a.num_blocks) {
+    if (c == 0) raise_device_error(2);
+    return;
+  }
+  const int64_t dst = (((int64_t)blk * a.H_kv + h) * 16 + (p & 15)) * a.d + 8 * c;
+  const int64_t src = row * a.d + 8 * c;
+  uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kw[e >> 2] |= f32_to_e4m3(in_to_f32<TIN>(a.k_new, src + e) * a.k_inv) << (8 * (e & 3));
+    vw[e >> 2] |= f32_to_e4m3(in_to_f32<TIN>(a.v_new, src + e) * a.v_inv) << (8 * (e & 3));
+  }
+  *reinterpret_cast<uint2*>(a.k_pool + dst) = make_uint2(kw[0], kw[1]);
+  *reinterpret_cast<uint2*>(a.v_pool + dst) = make_uint2(vw[0], vw[1]);
+}
+
 }  // namespace attn

@@ -33,6 +33,7 @@ from .attention import (one_shot, softmax_weights, tiled, splitk_merge, attentio
 from .brute import brute_attention
 from .caches import ListCache, ContigCache, PagedCache
 from .decode import cached_decode, naive_decode, decode_step, chunk_step
+from .fp8 import E4M3_VALUES, e4m3_round, e4m3_value, quantize, decode_step_fp8
 
 __all__ = [
     "decode_bits", "kv_bytes", "kv_head_of",
@@ -40,4 +41,5 @@ __all__ = [
     "brute_attention",
     "ListCache", "ContigCache", "PagedCache",
     "cached_decode", "naive_decode", "decode_step", "chunk_step",
+    "E4M3_VALUES", "e4m3_round", "e4m3_value", "quantize", "decode_step_fp8",
 ]
