@@ -10,7 +10,9 @@ One step runs every stage of the path once, each on its own workload:
                H_kv=8, d=128, cached lengths uniform in [1024, 32768];
   * chunk    : kv_append of 512 new tokens per sequence + attn_prefill_paged
                (chunked prefill against the paged cache), bf16, B=16, H_q=32,
-               H_kv=8, d=128, cached prefixes uniform in [0, 4096].
+               H_kv=8, d=128, cached prefixes uniform in [0, 4096];
+  * fp8      : kv_append_fp8 + attn_decode_paged_fp8, the paged workload with
+               the cache stored as OCP FP8 E4M3 (KV GB/s counts 1-byte values).
 Inputs are seeded synthetic tensors already resident in HBM.  Each kernel call
 is bracketed by HIP events on the stream it runs on.
 
@@ -188,10 +190,21 @@ def main() -> int:
     k_flops = synth.chunk_flops(kinp["lens"], kcase.n_new, kcase.H_q, kcase.d, causal=True)
     del kinp
     log(f"chunk prefill inputs ready ({time.perf_counter() - t_gen:.1f} s)")
+
+    # the paged decode workload over an 8-bit (FP8 E4M3) cache: same q, new rows,
+    # lengths, block table and workspace as the bf16 paged leg
+    fcase = gcase
+    finp = synth.fp8_decode_inputs(fcase, base=ginp)
+    f_kp = torch.from_numpy(finp["k_pool"]).cuda()
+    f_vp = torch.from_numpy(finp["v_pool"]).cuda()
+    f_out = torch.empty_like(g["q"])
+    f_bytes = int(np.sum((finp["lens"] + fcase.n_new).astype(np.int64))) * fcase.H_kv * fcase.d * 2  # 1 byte each
+    del finp
+    log(f"fp8 decode inputs ready ({time.perf_counter() - t_gen:.1f} s)")
     torch.cuda.synchronize()
 
     legs = ["prefill", "paged_append", "paged_decode", "contig_append", "contig_decode", "chunk_append",
-            "chunk_prefill"]
+            "chunk_prefill", "fp8_append", "fp8_decode"]
 
     def step(ev=None):
         def rec(i):
@@ -215,6 +228,11 @@ def main() -> int:
         K.attn_prefill_paged(kd["q"], kd["k_pool"], kd["v_pool"], k_table, k_lens, causal=True,
                              scale=kcase.sm_scale, return_lse=True, out=k_out, lse=k_lse)
         rec(7)
+        K.kv_append_fp8(f_kp, f_vp, g["k_new"], g["v_new"], g_lens, g_table, 0.5, 0.5)
+        rec(8)
+        K.attn_decode_paged_fp8(g["q"], f_kp, f_vp, g_table, g_seq, k_scale=0.5, v_scale=0.5,
+                                scale=fcase.sm_scale, workspace=g_ws, out=f_out)
+        rec(9)
 
     if args.calibrate_copy:
         # torch's elementwise multiply: reads 2^30 bytes, writes 2^30 bytes per launch
@@ -253,6 +271,7 @@ def main() -> int:
     g_gbs = g_bytes / (ms["paged_decode"] * 1e-3) / 1e9
     c_gbs = c_bytes / (ms["contig_decode"] * 1e-3) / 1e9
     k_tflops = k_flops / (ms["chunk_prefill"] * 1e-3) / 1e12
+    f_gbs = f_bytes / (ms["fp8_decode"] * 1e-3) / 1e9
 
     def roof(bound, achieved, peak, unit, kernel, per_unit):
         return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -296,6 +315,14 @@ def main() -> int:
             "append_ms": round(ms["chunk_append"], 4),
             "roofline": roof("mfma", k_tflops, PEAK_BF16_TFLOPS, "TFLOP/s",
                              "prefill_mfma_kernel<BF16,128,causal,paged>", {"flops": k_flops}),
+        },
+        "decode_paged_fp8": {
+            "value": round(f_gbs, 1), "unit": "GB/s", "workload": fcase.name + " (E4M3 cache)",
+            "kv_bytes": f_bytes, "ms_mean": round(ms["fp8_decode"], 4), "ms_median": round(med["fp8_decode"], 4),
+            "append_ms": round(ms["fp8_append"], 4),
+            "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["fp8_decode"], 3),
+            "roofline": roof("hbm", f_gbs, PEAK_HBM_GBS, "GB/s", "decode_mfma_kernel<BF16,128,paged,fp8>+merge",
+                             {"bytes": f_bytes}),
         },
         "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
         "device_error_flags": flags,
