@@ -34,6 +34,7 @@ from .brute import brute_attention
 from .caches import ListCache, ContigCache, PagedCache
 from .decode import cached_decode, naive_decode, decode_step, chunk_step
 from .fp8 import E4M3_VALUES, e4m3_round, e4m3_value, quantize, decode_step_fp8
+from .block_pool import FreeListPool, NoBlocks, blocks_for, simulate
 
 __all__ = [
     "decode_bits", "kv_bytes", "kv_head_of",
@@ -42,4 +43,5 @@ __all__ = [
     "ListCache", "ContigCache", "PagedCache",
     "cached_decode", "naive_decode", "decode_step", "chunk_step",
     "E4M3_VALUES", "e4m3_round", "e4m3_value", "quantize", "decode_step_fp8",
+    "FreeListPool", "NoBlocks", "blocks_for", "simulate",
 ]

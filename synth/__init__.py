@@ -339,3 +339,34 @@ def tiny_decode_steps(case: PrefillCase = TINY_PREFILL, steps: int = TINY_DECODE
 def kv_bytes_read(lens_after: np.ndarray, H_kv: int, d: int, dtype: str) -> int:
     """Bytes of K and V one decode step must read: every valid token, both tensors."""
     return int(np.sum(lens_after.astype(np.int64))) * H_kv * d * 2 * ELEM_BYTES[dtype]
+
+
+# --------------------------------------------------------------------------
+# chat-completion lengths for the block-pool serving simulation
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class ChatCase:
+    name: str
+    n_requests: int
+    prompt_lo: int
+    prompt_hi: int
+    output_lo: int
+    output_hi: int
+    max_len: int
+    memory_tokens: int
+    seed: int
+
+
+# 1,000 chat completions of different lengths ("KV缓存与Flash注意力", 练习); memory
+# for 64 contiguous max_len reservations of 2,048 tokens.
+CHAT_SIM = ChatCase("chat_sim_1000_prompt16-1024_out16-1024_max2048_mem131072",
+                    1000, 16, 1024, 16, 1024, 2048, 64 * 2048, 11)
+
+
+def chat_requests(case: ChatCase = CHAT_SIM):
+    """Prompt and output lengths (int64 arrays), each uniform over its inclusive
+    range, drawn from ``SFC64(case.seed)``: all prompts, then all outputs."""
+    rng = make_rng(case.seed)
+    prompts = rng.integers(case.prompt_lo, case.prompt_hi + 1, size=case.n_requests)
+    outputs = rng.integers(case.output_lo, case.output_hi + 1, size=case.n_requests)
+    return prompts.astype(np.int64), outputs.astype(np.int64)
