@@ -11,7 +11,8 @@
  *
  * Conventions shared by every call
  * --------------------------------
- *  - Every tensor pointer is a DEVICE pointer owned by the caller.  Tensors are
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller (the block
+ *    pool calls at the end are the exception: they work on host memory only).  Tensors are
  *    dense, row-major (C order) and 16-byte aligned.  The library never
  *    allocates, frees or keeps a pointer after a call returns.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
@@ -47,7 +48,8 @@ enum attn_status {
   ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, H_q % H_kv != 0, misalignment */
   ATTN_ERR_UNSUPPORTED = 2, /* dtype, head dimension or block size not built      */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required          */
-  ATTN_ERR_HIP = 4          /* the HIP runtime refused a launch                    */
+  ATTN_ERR_HIP = 4,         /* the HIP runtime refused a launch                    */
+  ATTN_ERR_NO_BLOCKS = 5    /* a block pool cannot meet a reservation              */
 };
 
 /* Device error flags raised by kernels (bitwise OR), see attn_device_error_flags. */
@@ -224,6 +226,28 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
                           float k_scale, float v_scale, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * kv_copy_blocks -- copy whole physical blocks of the K and V pools.
+ *
+ * The device half of copy on write: when a sequence forked from a shared
+ * prompt (attn_block_pool_fork) first writes into the prompt's partly filled
+ * last block, attn_block_pool_reserve hands it a fresh block and reports the
+ * (old, new) pair; this call copies the old block's K and V into the new one
+ * ("KV缓存与Flash注意力", 练习: one pass over the prompt fills the cache, and
+ * every completion branches from it).
+ *
+ *   pairs : device int32 [n_pairs][2] = (src, dst); n_pairs in [0, 65535].
+ *           The dst blocks must be distinct and must not be a src of the same
+ *           call (fresh blocks from the pool always are).
+ *   pools : [num_blocks, H_kv, 16, d] elements of elem_bytes bytes (1 for the
+ *           FP8 pools, 2 for f16/bf16, 4 for f32); every KV head of a block is
+ *           copied.
+ * An id outside [0, num_blocks) skips its pair and raises ATTN_DEVERR_BAD_BLOCK.
+ * Errors: INVALID_ARG, UNSUPPORTED (d, elem_bytes, block_size != 16), HIP.
+ */
+int kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n_pairs, int H_kv, int d,
+                   int block_size, int num_blocks, int elem_bytes, void* stream);
+
 /* Workspace bytes attn_decode / attn_decode_paged need for a cache capacity of
  * max_seq_len tokens per sequence.  0 on invalid sizes. */
 size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d);
@@ -237,6 +261,71 @@ const char* attn_version(void);
 /* Reads and clears the device error flags (enum attn_device_error) of the current
  * device after synchronising `stream`.  Returns the flags, or -1 if HIP failed. */
 int attn_device_error_flags(void* stream);
+
+/*
+ * Block pool -- host bookkeeping of the paged pools' physical blocks.
+ *
+ * The cache is cut into 16-token blocks, a block table maps each sequence's
+ * logical blocks to physical ones, and a finished sequence's blocks are reused
+ * at once ("KV Cache:推理慢的真正原因", 工程优化手段 / 1).  Blocks come from a
+ * free list and go back to it when a sequence finishes ("KV缓存与Flash注意力",
+ * 练习).  Forked sequences share blocks; each block counts its holders and
+ * returns to the free list when the count reaches zero.
+ *
+ * Free-list order: a stack.  Initially block 0 is on top, then 1, 2, ...; a
+ * freed block goes on top, so the most recently freed block is reused first.
+ *
+ * All pointers here are HOST pointers; a row is one sequence's block-table row
+ * (int32, max_blocks entries, -1 = unassigned), the layout attn_decode_paged
+ * reads once copied to the device.  Row entry j holds tokens 16j .. 16j+15.
+ * Every call checks all its arguments before it changes anything, so a failed
+ * call leaves the pool and the rows as they were.  A pool is not thread-safe:
+ * calls on one pool must not overlap.
+ */
+typedef struct attn_block_pool attn_block_pool;
+
+/* A pool of num_blocks free blocks; NULL (and attn_last_error) if num_blocks < 1. */
+attn_block_pool* attn_block_pool_create(int num_blocks);
+
+/* Frees the pool's host memory; NULL is a no-op. */
+void attn_block_pool_destroy(attn_block_pool* pool);
+
+/* Number of free blocks; -1 for a NULL pool. */
+int attn_block_pool_free_blocks(const attn_block_pool* pool);
+
+/* Number of sequences holding `block`; -1 for a NULL pool or an id out of range. */
+int attn_block_pool_holders(const attn_block_pool* pool, int block);
+
+/* Grow a sequence holding cur_len tokens so its row covers new_len tokens:
+ * entries ceil(cur_len/16) .. ceil(new_len/16)-1 receive blocks from the free
+ * list.  Copy on write: if new_len > cur_len, cur_len is not a multiple of 16
+ * and the block holding token cur_len is shared, the row gets a fresh block in
+ * its place and copy_pair[0..1] = (old, new) (the caller copies the contents
+ * with kv_copy_blocks before appending); otherwise copy_pair = (-1, -1).
+ * Errors: INVALID_ARG (null pointers, 0 <= cur_len <= new_len <= 16*max_blocks
+ *         violated, or the row's first ceil(cur_len/16) entries not held blocks),
+ *         NO_BLOCKS (too few free blocks: nothing changes). */
+int attn_block_pool_reserve(attn_block_pool* pool, int32_t* row, int max_blocks, int cur_len, int new_len,
+                            int32_t* copy_pair);
+
+/* attn_block_pool_reserve for sequences b = 0 .. B-1 in order, rows of
+ * `table` [B][max_blocks].  Copy pairs are written densely to copy_pairs
+ * [B][2] and counted in *n_copies.  *n_done = the number of sequences reserved;
+ * on an error the sequences from *n_done on are unchanged (the caller can free
+ * blocks, e.g. by preempting a sequence, and continue from there). */
+int attn_block_pool_reserve_batch(attn_block_pool* pool, int32_t* table, int B, int max_blocks,
+                                  const int32_t* cur_lens, const int32_t* new_lens, int32_t* copy_pairs,
+                                  int* n_copies, int* n_done);
+
+/* Drop a sequence of len tokens: each of its first ceil(len/16) blocks loses a
+ * holder (in row order; a block left with none goes on top of the free list)
+ * and the entries become -1.  Errors: INVALID_ARG. */
+int attn_block_pool_release(attn_block_pool* pool, int32_t* row, int max_blocks, int len);
+
+/* Fork: dst's first ceil(len/16) entries become src's blocks, each gaining a
+ * holder.  dst should hold no blocks in those entries (they are overwritten).
+ * Errors: INVALID_ARG. */
+int attn_block_pool_fork(attn_block_pool* pool, const int32_t* src, int32_t* dst, int max_blocks, int len);
 
 #ifdef __cplusplus
 }

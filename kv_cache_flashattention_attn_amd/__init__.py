@@ -10,6 +10,8 @@ streams only.
     kv_append(k_cache, v_cache, k_new, v_new, cache_lens, block_table=None, num_blocks=None)
     attn_decode(q, k_cache, v_cache, seq_lens, scale=None, return_lse=False, workspace=None)
     attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale=None, ...)
+    kv_copy_blocks(k_pool, v_pool, pairs)
+    BlockPool (block_pool.py): the host block pool's calls
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ import torch
 
 __all__ = [
     "AttnError", "lib", "lib_path", "attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode",
-    "attn_decode_paged", "kv_append_fp8", "attn_decode_paged_fp8",
+    "attn_decode_paged", "kv_append_fp8", "attn_decode_paged_fp8", "kv_copy_blocks",
     "attn_decode_workspace_bytes", "attn_device_error_flags", "attn_version", "DTYPE_CODES",
     "EXPORTED_SYMBOLS",
 ]
@@ -33,11 +35,14 @@ lib_path = os.path.join(_PKG, "libattn.so")
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
-          4: "ATTN_ERR_HIP"}
+          4: "ATTN_ERR_HIP", 5: "ATTN_ERR_NO_BLOCKS"}
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
-                    "kv_append_fp8", "attn_decode_paged_fp8",
+                    "kv_append_fp8", "attn_decode_paged_fp8", "kv_copy_blocks",
                     "attn_decode_workspace_bytes", "attn_last_error", "attn_version",
-                    "attn_device_error_flags")
+                    "attn_device_error_flags",
+                    "attn_block_pool_create", "attn_block_pool_destroy", "attn_block_pool_free_blocks",
+                    "attn_block_pool_holders", "attn_block_pool_reserve", "attn_block_pool_reserve_batch",
+                    "attn_block_pool_release", "attn_block_pool_fork")
 
 
 class AttnError(RuntimeError):
@@ -74,8 +79,21 @@ def lib() -> ctypes.CDLL:
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_version.restype = ctypes.c_char_p
     L.attn_device_error_flags.argtypes = [vp]
+    L.kv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.attn_block_pool_create.argtypes = [i32]
+    L.attn_block_pool_create.restype = vp
+    L.attn_block_pool_destroy.argtypes = [vp]
+    L.attn_block_pool_destroy.restype = None
+    L.attn_block_pool_free_blocks.argtypes = [vp]
+    L.attn_block_pool_holders.argtypes = [vp, i32]
+    L.attn_block_pool_reserve.argtypes = [vp, vp, i32, i32, i32, vp]
+    L.attn_block_pool_reserve_batch.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    L.attn_block_pool_release.argtypes = [vp, vp, i32, i32]
+    L.attn_block_pool_fork.argtypes = [vp, vp, vp, i32, i32]
     for name in ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
-                 "kv_append_fp8", "attn_decode_paged_fp8", "attn_device_error_flags"):
+                 "kv_append_fp8", "attn_decode_paged_fp8", "attn_device_error_flags", "kv_copy_blocks",
+                 "attn_block_pool_free_blocks", "attn_block_pool_holders", "attn_block_pool_reserve",
+                 "attn_block_pool_reserve_batch", "attn_block_pool_release", "attn_block_pool_fork"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -289,3 +307,16 @@ def attn_device_error_flags() -> int:
 
 def attn_version() -> str:
     return lib().attn_version().decode()
+
+
+def kv_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor) -> None:
+    """Copy whole blocks of both pools ([num_blocks, H_kv, 16, d], any element
+    size) for each (src, dst) row of the device int32 tensor ``pairs`` [n, 2]."""
+    nb, H_kv, bs, d = k_pool.shape
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool must match")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    rc = lib().kv_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(pairs, "pairs", torch.int32),
+                              pairs.shape[0], H_kv, d, bs, nb, k_pool.element_size(), _stream())
+    _check("kv_copy_blocks", rc)

@@ -4,6 +4,7 @@
 // device error flag (common.h) without relocatable device code.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -12,6 +13,7 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "block_pool.h"
 #include "common.h"
 #include "decode_mfma.h"
 #include "decode_plain.h"
@@ -476,6 +478,143 @@ int kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_n
     default: hipLaunchKernelGGL(attn::kv_append_fp8_kernel<attn::BF16>, grid, dim3(256), 0, st, a); break;
   }
   return launch_status("kv_append_fp8");
+}
+
+int kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n_pairs, int H_kv, int d, int block_size,
+                   int num_blocks, int elem_bytes, void* stream) {
+  if (n_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !pairs) return fail(ATTN_ERR_INVALID_ARG, "kv_copy_blocks: null pointer");
+  if (n_pairs < 0 || n_pairs > 65535)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_copy_blocks: n_pairs must be in [0, 65535] (got %d)", n_pairs);
+  if (H_kv < 1 || num_blocks < 1) return fail(ATTN_ERR_INVALID_ARG, "kv_copy_blocks: H_kv, num_blocks must be >= 1");
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "kv_copy_blocks: block_size must be 16 (got %d)", block_size);
+  if (!plain_head_dim(d)) return fail(ATTN_ERR_UNSUPPORTED, "kv_copy_blocks: head dim %d not supported", d);
+  if (!(elem_bytes == 1 || elem_bytes == 2 || elem_bytes == 4))
+    return fail(ATTN_ERR_UNSUPPORTED, "kv_copy_blocks: elem_bytes must be 1, 2 or 4 (got %d)", elem_bytes);
+  if (!aligned16(k_pool) || !aligned16(v_pool) || (reinterpret_cast<uintptr_t>(pairs) & 7u))
+    return fail(ATTN_ERR_INVALID_ARG, "kv_copy_blocks: pools must be 16-byte and pairs 8-byte aligned");
+  const int64_t chunks = (int64_t)H_kv * 16 * d * elem_bytes / 16;
+  attn::CopyBlocksArgs a{static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), pairs, chunks, num_blocks};
+  const int64_t gx = std::min<int64_t>((chunks + 255) / 256, 64);
+  hipLaunchKernelGGL(attn::kv_copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n_pairs), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_status("kv_copy_blocks");
+}
+
+// ---- host block pool -------------------------------------------------------
+
+attn_block_pool* attn_block_pool_create(int num_blocks) {
+  if (num_blocks < 1) {
+    fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_create: num_blocks must be >= 1 (got %d)", num_blocks);
+    return nullptr;
+  }
+  try {
+    auto* p = reinterpret_cast<attn_block_pool*>(new attn::BlockPool(num_blocks));
+    ok();
+    return p;
+  } catch (...) {
+    fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_create: out of host memory");
+    return nullptr;
+  }
+}
+
+void attn_block_pool_destroy(attn_block_pool* pool) { delete reinterpret_cast<attn::BlockPool*>(pool); }
+
+int attn_block_pool_free_blocks(const attn_block_pool* pool) {
+  if (!pool) return -1;
+  return (int)reinterpret_cast<const attn::BlockPool*>(pool)->free_stack.size();
+}
+
+int attn_block_pool_holders(const attn_block_pool* pool, int block) {
+  if (!pool) return -1;
+  const auto* p = reinterpret_cast<const attn::BlockPool*>(pool);
+  if (block < 0 || block >= p->num_blocks()) return -1;
+  return p->holders[block];
+}
+
+int attn_block_pool_reserve(attn_block_pool* pool, int32_t* row, int max_blocks, int cur_len, int new_len,
+                            int32_t* copy_pair) {
+  if (!pool || !row || !copy_pair) return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_reserve: null pointer");
+  auto* p = reinterpret_cast<attn::BlockPool*>(pool);
+  if (max_blocks < 1 || cur_len < 0 || new_len < cur_len || attn::pool_blocks_for(new_len) > max_blocks)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_reserve: need 0 <= cur_len (%d) <= new_len (%d) <= 16 * %d",
+                cur_len, new_len, max_blocks);
+  if (!p->row_ok(row, cur_len))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_reserve: the row's first %d entries are not held blocks",
+                attn::pool_blocks_for(cur_len));
+  const int have = attn::pool_blocks_for(cur_len), want = attn::pool_blocks_for(new_len);
+  const bool cow = new_len > cur_len && cur_len % attn::kPoolBlockTokens != 0 && p->holders[row[have - 1]] > 1;
+  const int need = want - have + (cow ? 1 : 0);
+  if (need > (int)p->free_stack.size())
+    return fail(ATTN_ERR_NO_BLOCKS, "attn_block_pool_reserve: %d blocks needed, %d free", need,
+                (int)p->free_stack.size());
+  copy_pair[0] = copy_pair[1] = -1;
+  if (cow) {
+    const int32_t old = row[have - 1];
+    const int32_t fresh = p->take();
+    p->drop(old);  // another sequence still holds it
+    row[have - 1] = fresh;
+    copy_pair[0] = old;
+    copy_pair[1] = fresh;
+  }
+  for (int j = have; j < want; ++j) row[j] = p->take();
+  return ok();
+}
+
+int attn_block_pool_reserve_batch(attn_block_pool* pool, int32_t* table, int B, int max_blocks,
+                                  const int32_t* cur_lens, const int32_t* new_lens, int32_t* copy_pairs,
+                                  int* n_copies, int* n_done) {
+  if (!pool || !table || !cur_lens || !new_lens || !copy_pairs || !n_copies || !n_done)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_reserve_batch: null pointer");
+  if (B < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_reserve_batch: B < 0");
+  *n_copies = 0;
+  *n_done = 0;
+  for (int b = 0; b < B; ++b) {
+    int32_t pair[2];
+    const int rc = attn_block_pool_reserve(pool, table + (int64_t)b * max_blocks, max_blocks, cur_lens[b],
+                                           new_lens[b], pair);
+    if (rc != ATTN_OK) return rc;
+    if (pair[0] >= 0) {
+      copy_pairs[2 * *n_copies] = pair[0];
+      copy_pairs[2 * *n_copies + 1] = pair[1];
+      ++*n_copies;
+    }
+    *n_done = b + 1;
+  }
+  return ok();
+}
+
+int attn_block_pool_release(attn_block_pool* pool, int32_t* row, int max_blocks, int len) {
+  if (!pool || !row) return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_release: null pointer");
+  auto* p = reinterpret_cast<attn::BlockPool*>(pool);
+  if (max_blocks < 1 || len < 0 || attn::pool_blocks_for(len) > max_blocks)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_release: need 0 <= len (%d) <= 16 * %d", len, max_blocks);
+  if (!p->row_ok(row, len))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_release: the row's first %d entries are not held blocks",
+                attn::pool_blocks_for(len));
+  const int nb = attn::pool_blocks_for(len);
+  for (int j = 0; j < nb; ++j) {
+    p->drop(row[j]);
+    row[j] = -1;
+  }
+  return ok();
+}
+
+int attn_block_pool_fork(attn_block_pool* pool, const int32_t* src, int32_t* dst, int max_blocks, int len) {
+  if (!pool || !src || !dst) return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_fork: null pointer");
+  auto* p = reinterpret_cast<attn::BlockPool*>(pool);
+  if (max_blocks < 1 || len < 0 || attn::pool_blocks_for(len) > max_blocks)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_fork: need 0 <= len (%d) <= 16 * %d", len, max_blocks);
+  if (!p->row_ok(src, len))
+    return fail(ATTN_ERR_INVALID_ARG, "attn_block_pool_fork: the source row's first %d entries are not held blocks",
+                attn::pool_blocks_for(len));
+  const int nb = attn::pool_blocks_for(len);
+  for (int j = 0; j < nb; ++j) {
+    dst[j] = src[j];
+    ++p->holders[src[j]];
+  }
+  return ok();
 }
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }

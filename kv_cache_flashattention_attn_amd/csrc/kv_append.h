@@ -166,4 +166,35 @@ __global__ void __launch_bounds__(256) kv_append_fp8_kernel(AppendFp8Args a) {
   *reinterpret_cast<uint2*>(a.v_pool + dst) = make_uint2(vw[0], vw[1]);
 }
 
+// kv_copy_blocks: duplicate whole physical blocks (every KV head) of the K and V
+// pools, the copy half of copy on write when a sequence forked from a shared
+// prompt first writes into the prompt's partly filled last block
+// ("KV缓存与Flash注意力", 练习, prompts whose cache is shared by the completions
+// that branch from it).  blockIdx.y picks the (src, dst) pair; the x dimension
+// walks the block in 16-byte chunks, so each wave moves 1 KiB contiguous.
+struct CopyBlocksArgs {
+  uint4* k_pool;
+  uint4* v_pool;
+  const int32_t* pairs;      // [n_pairs][2] = (src, dst)
+  int64_t chunks_per_block;  // H_kv * 16 * row bytes / 16
+  int num_blocks;
+};
+
+__global__ void __launch_bounds__(256) kv_copy_blocks_kernel(CopyBlocksArgs a) {
+  const int src = a.pairs[2 * blockIdx.y];
+  const int dst = a.pairs[2 * blockIdx.y + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) raise_device_error(2);
+    return;
+  }
+  const int64_t s0 = (int64_t)src * a.chunks_per_block, d0 = (int64_t)dst * a.chunks_per_block;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < a.chunks_per_block;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const uint4 k = a.k_pool[s0 + c];
+    const uint4 v = a.v_pool[s0 + c];
+    a.k_pool[d0 + c] = k;
+    a.v_pool[d0 + c] = v;
+  }
+}
+
 }  // namespace attn
