@@ -80,6 +80,40 @@ def blas_threads() -> int:
         return 1
 
 
+def block_pool_leg() -> dict:
+    """Host side of the paged cache: the serving simulation on the chat workload
+    (contiguous max_len reservations vs 16-token blocks from the native pool)
+    and the native pool's cost per sequence-step of reserve_batch."""
+    import synth
+    from kv_cache_flashattention_attn_amd import serving_sim
+    from kv_cache_flashattention_attn_amd.block_pool import BlockPool
+
+    c = synth.CHAT_SIM
+    prompts, outputs = synth.chat_requests(c)
+    t0 = time.perf_counter()
+    sims = {s: serving_sim.simulate(prompts, outputs, c.memory_tokens, c.max_len, s)
+            for s in ("contiguous", "paged")}
+    sim_s = time.perf_counter() - t0
+    B, steps = 256, 2048
+    mb = steps // 16 + 1
+    pool = BlockPool(B * mb)
+    table = np.full((B, mb), -1, np.int32)
+    lens = np.zeros(B, np.int32)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pool.reserve_batch(table, lens, lens + 1)
+        lens += 1
+    dt = time.perf_counter() - t0
+    keep = ("utilization_held", "utilization_budget", "mean_running", "peak_running", "steps", "preemptions")
+    out = {"workload": c.name, "sim_seconds": round(sim_s, 2),
+           "reserve_ns_per_sequence_step": round(dt / (B * steps) * 1e9, 1),
+           "reserve_batch": f"{steps} steps x {B} sequences, one token each"}
+    for s, r in sims.items():
+        out[s] = {k: (round(r[k], 4) if isinstance(r[k], float) else r[k]) for k in keep}
+    out["concurrency_gain"] = round(sims["paged"]["mean_running"] / sims["contiguous"]["mean_running"], 3)
+    return out
+
+
 def cpu_baseline(seconds: float, prefill_case, prefill_raw, paged_case, paged_inp):
     """The fp64 oracle as it stands, on a bounded sample of the same workloads."""
     import oracle
@@ -328,6 +362,7 @@ def main() -> int:
         "device_error_flags": flags,
         "kernel_source_hash": kernel_source_hash(),
     }
+    result["block_pool"] = block_pool_leg()
     if args.cpu_seconds > 0:
         log("timing the CPU oracle on a bounded sample ...")
         cb = cpu_baseline(args.cpu_seconds, pcase, praw, gcase, ginp)
