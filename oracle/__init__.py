@@ -35,6 +35,7 @@ from .caches import ListCache, ContigCache, PagedCache
 from .decode import cached_decode, naive_decode, decode_step, chunk_step
 from .fp8 import E4M3_VALUES, e4m3_round, e4m3_value, quantize, decode_step_fp8
 from .block_pool import FreeListPool, NoBlocks, blocks_for, simulate
+from .int8 import quantize_int8, dequantize_int8, decode_step_int8
 
 __all__ = [
     "decode_bits", "kv_bytes", "kv_head_of",
@@ -44,4 +45,5 @@ __all__ = [
     "cached_decode", "naive_decode", "decode_step", "chunk_step",
     "E4M3_VALUES", "e4m3_round", "e4m3_value", "quantize", "decode_step_fp8",
     "FreeListPool", "NoBlocks", "blocks_for", "simulate",
+    "quantize_int8", "dequantize_int8", "decode_step_int8",
 ]

@@ -321,6 +321,43 @@ def fp8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
     return out
 
 
+def int8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
+                       base: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
+    """Inputs of one decode step over an int8 paged cache with per-channel scales.
+
+    Lengths, block table, q and the new token's K/V rows (in ``case.dtype``) are
+    those of ``decode_inputs(case, lens)`` (or of ``base``).  From
+    ``SFC64(case.seed + 8000)``, in this order:
+
+    * ``k_scales``, ``v_scales`` [H_kv, d] float32: 2^u with u uniform in
+      [-7, -4], and in every KV head 4 random channels of K multiplied by 16
+      (outlier key channels);
+    * the pools' codes: K's whole pool then V's, uniform integers in
+      [-127, 127] where a slot holds a cached token; slots holding none carry
+      K = 0 and V = 127 (the largest code).
+    """
+    out = dict(base) if base is not None else decode_inputs(case, lens=lens)
+    lens = out["lens"]
+    table = out["block_table"]
+    nblk, Hk, bs, d = out["k_pool"].shape
+    rng = make_rng(case.seed + 8000)
+    ks = np.exp2(rng.uniform(-7.0, -4.0, size=(Hk, d))).astype(np.float32)
+    for h in range(Hk):
+        ks[h, rng.choice(d, size=4, replace=False)] *= np.float32(16.0)
+    vs = np.exp2(rng.uniform(-7.0, -4.0, size=(Hk, d))).astype(np.float32)
+    held = np.zeros((nblk, bs), dtype=bool)
+    for b in range(case.B):
+        L = int(lens[b])
+        nb = -(-L // BLOCK_SIZE)
+        fill = np.clip(L - BLOCK_SIZE * np.arange(nb), 0, BLOCK_SIZE)
+        held[table[b, :nb]] = np.arange(bs)[None, :] < fill[:, None]
+    mask = held[:, None, :, None]
+    kp = np.where(mask, rng.integers(-127, 128, size=(nblk, Hk, bs, d), dtype=np.int8), np.int8(0))
+    vp = np.where(mask, rng.integers(-127, 128, size=(nblk, Hk, bs, d), dtype=np.int8), np.int8(127))
+    out.update(k_pool=kp.astype(np.int8), v_pool=vp.astype(np.int8), k_scales=ks, v_scales=vs)
+    return out
+
+
 def tiny_decode_steps(case: PrefillCase = TINY_PREFILL, steps: int = TINY_DECODE_STEPS):
     """The tiny case's decode phase: per step a query [B,H,d] and one new K/V row.
 
