@@ -227,6 +227,49 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kv_append_int8 / attn_decode_paged_int8 -- a paged KV cache stored as int8
+ * with one scale per (KV head, channel).
+ *
+ * Quantizing to int8 quarters the bytes of an fp32 cache and halves those of a
+ * 16-bit one; a few key channels hold very large values, and one scale for a
+ * whole tensor would magnify their error, so the scales are per channel ("KV
+ * Cache:推理慢的真正原因", 工程优化手段, the quantization item; int8 and int4
+ * caches are also named in "推理速度慢怎么办？KV Cache与Flash Attention如何加速大模型推理",
+ * section 三).  k_scales and v_scales are device fp32 [H_kv, d], > 0, fixed by
+ * the caller and shared by every token (equal entries give group scales):
+ *   stored = clamp(rint(x / s[h][c]), -127, 127)  -- x converted exactly to fp32,
+ *            the quotient rounded to fp32, rint ties to even; NaN -> 0
+ *   value  = stored * s[h][c]
+ * The pools are int8 [num_blocks, H_kv, 16, d]; block table and lengths as for
+ * kv_append / attn_decode_paged.
+ */
+/* Append n_new tokens' K/V ([B, H_kv, n_new, d] in `dtype`: F32, F16 or BF16),
+ * quantized, at positions cache_lens[b] ..; cache_lens is not advanced.
+ * Errors: INVALID_ARG (pointers, sizes, misaligned scale arrays),
+ *         UNSUPPORTED (dtype, d, block_size != 16), HIP. */
+int kv_append_int8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                   const int32_t* cache_lens, const int32_t* block_table,
+                   int B, int H_kv, int n_new, int d, int block_size,
+                   int max_blocks_per_seq, int num_blocks, int dtype,
+                   const float* k_scales, const float* v_scales, void* stream);
+
+/* attn_decode_paged over the int8 pools: q, o [B, H_q, d] in `dtype` (F16 or
+ * BF16), d = 64 or 128, scale > 0.  Same workspace as attn_decode_paged (its
+ * last two regions hold the query with the key scales folded in).  The scores
+ * are computed in f16 MFMAs: the codes are exact in f16, and the query times
+ * the key scales, rescaled per head by a power of two, is split into two f16
+ * parts (about 22 bits together), each multiplied with the codes.
+ * Errors: as attn_decode_paged; INVALID_ARG for null or misaligned scale arrays;
+ *         UNSUPPORTED for other dtypes / d. */
+int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           void* o, float* lse,
+                           int B, int H_q, int H_kv, int d, int block_size,
+                           int max_blocks_per_seq, int num_blocks, float scale,
+                           const float* k_scales, const float* v_scales, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kv_copy_blocks -- copy whole physical blocks of the K and V pools.
  *
  * The device half of copy on write: when a sequence forked from a shared
@@ -248,8 +291,13 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
 int kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n_pairs, int H_kv, int d,
                    int block_size, int num_blocks, int elem_bytes, void* stream);
 
-/* Workspace bytes attn_decode / attn_decode_paged need for a cache capacity of
- * max_seq_len tokens per sequence.  0 on invalid sizes. */
+/* Workspace bytes every decode call (attn_decode, attn_decode_paged and its
+ * 8-bit forms) needs for a cache capacity of max_seq_len tokens per sequence.
+ * Layout, each region 256-byte aligned: split partial outputs fp32
+ * [B][H_q][S][d], their lse fp32 [B][H_q][S], piece counts int32 [B][H_q],
+ * then (int8 cache only) the scaled query as two f16 parts [B][H_q][2][d] and
+ * its factors fp32 [B][H_q]; S = ceil(max_seq_len / 256) + 1.  0 on invalid
+ * sizes. */
 size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d);
 
 /* Message describing the last error returned on the calling thread ("" if none). */

@@ -24,7 +24,8 @@ import torch
 
 __all__ = [
     "AttnError", "lib", "lib_path", "attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode",
-    "attn_decode_paged", "kv_append_fp8", "attn_decode_paged_fp8", "kv_copy_blocks",
+    "attn_decode_paged", "kv_append_fp8", "attn_decode_paged_fp8", "kv_append_int8", "attn_decode_paged_int8",
+    "kv_copy_blocks",
     "attn_decode_workspace_bytes", "attn_device_error_flags", "attn_version", "DTYPE_CODES",
     "EXPORTED_SYMBOLS",
 ]
@@ -37,7 +38,8 @@ DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16:
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
           4: "ATTN_ERR_HIP", 5: "ATTN_ERR_NO_BLOCKS"}
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
-                    "kv_append_fp8", "attn_decode_paged_fp8", "kv_copy_blocks",
+                    "kv_append_fp8", "attn_decode_paged_fp8", "kv_append_int8", "attn_decode_paged_int8",
+                    "kv_copy_blocks",
                     "attn_decode_workspace_bytes", "attn_last_error", "attn_version",
                     "attn_device_error_flags",
                     "attn_block_pool_create", "attn_block_pool_destroy", "attn_block_pool_free_blocks",
@@ -80,6 +82,9 @@ def lib() -> ctypes.CDLL:
     L.attn_version.restype = ctypes.c_char_p
     L.attn_device_error_flags.argtypes = [vp]
     L.kv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.kv_append_int8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.attn_decode_paged_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp,
+                                         vp, i32, vp, sz, vp]
     L.attn_block_pool_create.argtypes = [i32]
     L.attn_block_pool_create.restype = vp
     L.attn_block_pool_destroy.argtypes = [vp]
@@ -92,6 +97,7 @@ def lib() -> ctypes.CDLL:
     L.attn_block_pool_fork.argtypes = [vp, vp, vp, i32, i32]
     for name in ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
                  "kv_append_fp8", "attn_decode_paged_fp8", "attn_device_error_flags", "kv_copy_blocks",
+                 "kv_append_int8", "attn_decode_paged_int8",
                  "attn_block_pool_free_blocks", "attn_block_pool_holders", "attn_block_pool_reserve",
                  "attn_block_pool_reserve_batch", "attn_block_pool_release", "attn_block_pool_fork"):
         getattr(L, name).restype = i32
@@ -320,3 +326,55 @@ def kv_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tens
     rc = lib().kv_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(pairs, "pairs", torch.int32),
                               pairs.shape[0], H_kv, d, bs, nb, k_pool.element_size(), _stream())
     _check("kv_copy_blocks", rc)
+
+
+def kv_append_int8(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   cache_lens: torch.Tensor, block_table: torch.Tensor, k_scales: torch.Tensor,
+                   v_scales: torch.Tensor) -> None:
+    """Quantize and append k_new, v_new [B, H_kv, n_new, d] into int8 pools
+    [num_blocks, H_kv, 16, d] with per-channel scales (device fp32 [H_kv, d])."""
+    B, H_kv, n_new, d = k_new.shape
+    nb, _, bs, _ = k_pool.shape
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
+        raise ValueError("int8 pools are torch.int8 tensors")
+    if k_scales.shape != (H_kv, d) or v_scales.shape != (H_kv, d):
+        raise ValueError("k_scales and v_scales must be [H_kv, d]")
+    rc = lib().kv_append_int8(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                              _dev(v_new, "v_new"), _dev(cache_lens, "cache_lens", torch.int32),
+                              _dev(block_table, "block_table", torch.int32), B, H_kv, n_new, d, bs,
+                              block_table.shape[1], nb, _code(k_new), _dev(k_scales, "k_scales", torch.float32),
+                              _dev(v_scales, "v_scales", torch.float32), _stream())
+    _check("kv_append_int8", rc)
+
+
+def attn_decode_paged_int8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+                           seq_lens: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
+                           scale: Optional[float] = None, return_lse: bool = False,
+                           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None):
+    """attn_decode_paged over int8 pools (torch.int8 [num_blocks, H_kv, 16, d])
+    with per-channel scales (device fp32 [H_kv, d])."""
+    B, H_q, d = q.shape
+    nb, H_kv, bs, _ = k_pool.shape
+    mbps = block_table.shape[1]
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
+        raise ValueError("int8 pools are torch.int8 tensors")
+    if k_scales.shape != (H_kv, d) or v_scales.shape != (H_kv, d):
+        raise ValueError("k_scales and v_scales must be [H_kv, d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = attn_decode_workspace_bytes(B, H_q, mbps * bs, d)
+    workspace = _workspace(workspace, nbytes, q.device)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    rc = lib().attn_decode_paged_int8(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                      _dev(block_table, "block_table", torch.int32),
+                                      _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
+                                      _dev(lse, "lse", torch.float32) if return_lse else 0,
+                                      B, H_q, H_kv, d, bs, mbps, nb, scale,
+                                      _dev(k_scales, "k_scales", torch.float32),
+                                      _dev(v_scales, "v_scales", torch.float32), _code(q),
+                                      _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                      _stream())
+    _check("attn_decode_paged_int8", rc)
+    return (out, lse) if return_lse else out

@@ -70,7 +70,7 @@ int splits_for(int capacity) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t lse_off, cnt_off, bytes;
+  size_t lse_off, cnt_off, q16_off, qfac_off, bytes;
 };
 
 WorkspaceLayout workspace_layout(int B, int H_q, int capacity, int d) {
@@ -78,7 +78,10 @@ WorkspaceLayout workspace_layout(int B, int H_q, int capacity, int d) {
   WorkspaceLayout w;
   w.lse_off = align_up((size_t)B * H_q * S * d * sizeof(float), 256);
   w.cnt_off = align_up(w.lse_off + (size_t)B * H_q * S * sizeof(float), 256);
-  w.bytes = w.cnt_off + (size_t)B * H_q * sizeof(int32_t);
+  // int8 cache only: the scaled query as two f16 parts [B][H_q][2][d] and its factors [B][H_q]
+  w.q16_off = align_up(w.cnt_off + (size_t)B * H_q * sizeof(int32_t), 256);
+  w.qfac_off = align_up(w.q16_off + (size_t)B * H_q * 2 * d * sizeof(uint16_t), 256);
+  w.bytes = w.qfac_off + (size_t)B * H_q * sizeof(float);
   return w;
 }
 
@@ -165,15 +168,27 @@ int launch_decode_plain(const attn::DecodeArgs& a, hipStream_t st) {
   return launch_status("attn_decode");
 }
 
-template <typename T, int D, bool PAGED, bool FP8>
-int launch_decode_mfma(const attn::DecodeArgs& a, int32_t* piece_cnt, hipStream_t st, float v_scale = 1.f) {
+// How the cache stores K and V: 16-bit (the query's type), FP8 E4M3 with one
+// scale per tensor, or int8 with one scale per (KV head, channel).
+struct CacheQuant {
+  int kind = attn::kKV16;
+  float k_scale = 1.f, v_scale = 1.f;              // FP8
+  const float* k_scales = nullptr;                 // int8: [H_kv][d], device
+  const float* v_scales = nullptr;
+  float* q_fac = nullptr;                          // int8: workspace [B][H_q]
+  uint16_t* q16 = nullptr;                         // int8: workspace [B][H_q][2][d] f16
+};
+
+template <typename T, int D, bool PAGED, int KV>
+int launch_decode_mfma(const attn::DecodeArgs& a, int32_t* piece_cnt, hipStream_t st,
+                       const CacheQuant& cq = CacheQuant()) {
   const int G = a.H_q / a.H_kv;
-  const attn::DecodeStreamArgs sa{a, piece_cnt, (G + 15) / 16, v_scale};
-  const void* kernel = reinterpret_cast<const void*>(&attn::decode_mfma_kernel<T, D, PAGED, FP8>);
+  const attn::DecodeStreamArgs sa{a, piece_cnt, (G + 15) / 16, cq.v_scale, cq.v_scales, cq.q_fac};
+  const void* kernel = reinterpret_cast<const void*>(&attn::decode_mfma_kernel<T, D, PAGED, KV>);
   static int grid = 0;  // one value per instantiation; every device here is an MI355X
   if (grid == 0) grid = resident_grid(kernel, 64 * attn::kDecWaves);
   if (grid <= 0) return fail(ATTN_ERR_HIP, "attn_decode: occupancy query failed");
-  hipLaunchKernelGGL((attn::decode_mfma_kernel<T, D, PAGED, FP8>), dim3(grid), dim3(64 * attn::kDecWaves), 0, st,
+  hipLaunchKernelGGL((attn::decode_mfma_kernel<T, D, PAGED, KV>), dim3(grid), dim3(64 * attn::kDecWaves), 0, st,
                      sa, a.seq_lens, a.table);
   return launch_status("attn_decode");
 }
@@ -192,7 +207,7 @@ template <typename T, int D, bool PAGED>
 int decode_typed(const attn::DecodeArgs& a, void* o, float* lse, bool mfma, int32_t* piece_cnt, hipStream_t st) {
   if constexpr ((D == 64 || D == 128) && !std::is_same<T, attn::F32>::value) {
     if (mfma) {
-      const int rc = launch_decode_mfma<T, D, PAGED, false>(a, piece_cnt, st);
+      const int rc = launch_decode_mfma<T, D, PAGED, attn::kKV16>(a, piece_cnt, st);
       if (rc != ATTN_OK) return rc;
       return launch_merge<T, D>(a, o, lse, 0, piece_cnt, st);
     }
@@ -226,14 +241,34 @@ int decode_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, int d
   return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: dtype %d not supported", dtype);
 }
 
-// FP8 paged cache: the MFMA decode reading E4M3 K/V, then the merge.
-template <typename T>
-int decode_fp8_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, float v_scale, int32_t* cnt,
-                        hipStream_t st) {
-  int rc = d == 64 ? launch_decode_mfma<T, 64, true, true>(a, cnt, st, v_scale)
-                   : launch_decode_mfma<T, 128, true, true>(a, cnt, st, v_scale);
+// 8-bit paged cache (FP8 or int8): the MFMA decode widening K/V in registers, then the merge.
+template <typename T, int KV>
+int decode_q8_typed(attn::DecodeArgs a, void* o, float* lse, int d, const CacheQuant& cq, int32_t* cnt,
+                    hipStream_t st) {
+  if (KV == attn::kKVInt8) {
+    // fold the key scales into an f16 copy of the query, which the decode reads instead
+    const int G = a.H_q / a.H_kv;
+    if (d == 64)
+      hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 64>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
+                         cq.k_scales, cq.q16, cq.q_fac, a.H_q, G);
+    else
+      hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 128>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
+                         cq.k_scales, cq.q16, cq.q_fac, a.H_q, G);
+    const int rc = launch_status("attn_decode int8 query");
+    if (rc != ATTN_OK) return rc;
+    a.q = cq.q16;
+  }
+  int rc = d == 64 ? launch_decode_mfma<T, 64, true, KV>(a, cnt, st, cq)
+                   : launch_decode_mfma<T, 128, true, KV>(a, cnt, st, cq);
   if (rc != ATTN_OK) return rc;
   return d == 64 ? launch_merge<T, 64>(a, o, lse, 0, cnt, st) : launch_merge<T, 128>(a, o, lse, 0, cnt, st);
+}
+
+template <typename T>
+int decode_q8_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, const CacheQuant& cq, int32_t* cnt,
+                       hipStream_t st) {
+  return cq.kind == attn::kKVFp8 ? decode_q8_typed<T, attn::kKVFp8>(a, o, lse, d, cq, cnt, st)
+                                 : decode_q8_typed<T, attn::kKVInt8>(a, o, lse, d, cq, cnt, st);
 }
 
 int check_decode_common(const char* fn, const void* q, const void* k, const void* v, const int32_t* lens,
@@ -367,16 +402,24 @@ size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d) {
 static int decode_common(const char* fn, bool paged, const void* q, const void* k, const void* v,
                          const int32_t* table, const int32_t* seq_lens, void* o, float* lse, int B, int H_q,
                          int H_kv, int capacity, int mbps, int num_blocks, int d, float scale, int dtype,
-                         void* workspace, size_t workspace_bytes_given, void* stream, bool fp8 = false,
-                         float k_scale = 1.f, float v_scale = 1.f) {
+                         void* workspace, size_t workspace_bytes_given, void* stream,
+                         const CacheQuant& cq = CacheQuant()) {
   int rc = check_decode_common(fn, q, k, v, seq_lens, o, B, H_q, H_kv, d, dtype, scale);
   if (rc != ATTN_OK) return rc;
-  if (fp8) {
+  const bool q8 = cq.kind != attn::kKV16;
+  if (q8) {
     if (!(dtype == ATTN_F16 || dtype == ATTN_BF16) || !(d == 64 || d == 128))
       return fail(ATTN_ERR_UNSUPPORTED, "%s: f16/bf16 queries with d = 64 or 128 only", fn);
     if (!(scale > 0.f)) return fail(ATTN_ERR_UNSUPPORTED, "%s: scale must be positive", fn);
-    if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+  }
+  if (cq.kind == attn::kKVFp8) {
+    if (!std::isfinite(cq.k_scale) || !std::isfinite(cq.v_scale) || !(cq.k_scale > 0.f) || !(cq.v_scale > 0.f))
       return fail(ATTN_ERR_INVALID_ARG, "%s: k_scale and v_scale must be finite and positive", fn);
+  }
+  if (cq.kind == attn::kKVInt8) {
+    if (!cq.k_scales || !cq.v_scales) return fail(ATTN_ERR_INVALID_ARG, "%s: null scale array", fn);
+    if (!aligned16(cq.k_scales) || !aligned16(cq.v_scales))
+      return fail(ATTN_ERR_INVALID_ARG, "%s: scale arrays must be 16-byte aligned", fn);
   }
   if (capacity < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: cache capacity must be >= 1", fn);
   const size_t need = workspace_bytes(B, H_q, capacity, d);
@@ -401,12 +444,16 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
   a.max_blocks_per_seq = mbps;
   a.num_blocks = num_blocks;
   a.s_max = S;
-  a.scale_log2 = scale * (fp8 ? k_scale : 1.f) * attn::kLog2e;
+  a.scale_log2 = scale * (cq.kind == attn::kKVFp8 ? cq.k_scale : 1.f) * attn::kLog2e;
   int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.cnt_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fp8)
-    return dtype == ATTN_BF16 ? decode_fp8_dispatch<attn::BF16>(a, o, lse, d, v_scale, cnt, st)
-                              : decode_fp8_dispatch<attn::F16>(a, o, lse, d, v_scale, cnt, st);
+  if (q8) {
+    CacheQuant cqw = cq;
+    cqw.q16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + lay.q16_off);
+    cqw.q_fac = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.qfac_off);
+    return dtype == ATTN_BF16 ? decode_q8_dispatch<attn::BF16>(a, o, lse, d, cqw, cnt, st)
+                              : decode_q8_dispatch<attn::F16>(a, o, lse, d, cqw, cnt, st);
+  }
   return paged ? decode_dispatch<true>(a, o, lse, d, dtype, scale, cnt, st)
                : decode_dispatch<false>(a, o, lse, d, dtype, scale, cnt, st);
 }
@@ -445,39 +492,101 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
     return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_fp8: max_blocks_per_seq and num_blocks must be >= 1");
   if ((long long)max_blocks_per_seq * 16 > 0x7FFFFFFFLL)
     return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_fp8: max_blocks_per_seq too large");
+  CacheQuant cq;
+  cq.kind = attn::kKVFp8;
+  cq.k_scale = k_scale;
+  cq.v_scale = v_scale;
   return decode_common("attn_decode_paged_fp8", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q,
                        H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
-                       workspace_bytes_given, stream, true, k_scale, v_scale);
+                       workspace_bytes_given, stream, cq);
 }
+
+int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d,
+                           int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                           const float* k_scales, const float* v_scales, int dtype, void* workspace,
+                           size_t workspace_bytes_given, void* stream) {
+  if (!block_table) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_int8: null block table");
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_int8: block_size must be 16 (got %d)", block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_int8: max_blocks_per_seq and num_blocks must be >= 1");
+  if ((long long)max_blocks_per_seq * 16 > 0x7FFFFFFFLL)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_int8: max_blocks_per_seq too large");
+  CacheQuant cq;
+  cq.kind = attn::kKVInt8;
+  cq.k_scales = k_scales;
+  cq.v_scales = v_scales;
+  return decode_common("attn_decode_paged_int8", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q,
+                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
+                       workspace_bytes_given, stream, cq);
+}
+
+}  // extern "C"
+
+namespace {
+
+int append_8bit(const char* fn, bool i8, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                const int32_t* cache_lens, const int32_t* block_table, int B, int H_kv, int n_new, int d,
+                int block_size, int max_blocks_per_seq, int num_blocks, int dtype, float k_scale, float v_scale,
+                const float* k_scales, const float* v_scales, void* stream) {
+  if (!k_pool || !v_pool || !k_new || !v_new || !cache_lens || !block_table)
+    return fail(ATTN_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (B < 1 || H_kv < 1 || n_new < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: B, H_kv, n_new must be >= 1", fn);
+  if (!valid_dtype(dtype)) return fail(ATTN_ERR_UNSUPPORTED, "%s: dtype %d not supported", fn, dtype);
+  if (!plain_head_dim(d)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d not supported", fn, d);
+  if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "%s: block_size must be 16 (got %d)", fn, block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "%s: max_blocks_per_seq and num_blocks must be >= 1", fn);
+  if (i8) {
+    if (!k_scales || !v_scales) return fail(ATTN_ERR_INVALID_ARG, "%s: null scale array", fn);
+    if (!aligned16(k_scales) || !aligned16(v_scales))
+      return fail(ATTN_ERR_INVALID_ARG, "%s: scale arrays must be 16-byte aligned", fn);
+  } else if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f)) {
+    return fail(ATTN_ERR_INVALID_ARG, "%s: k_scale and v_scale must be finite and positive", fn);
+  }
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(ATTN_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  attn::Append8Args a{static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_new, v_new, cache_lens,
+                      block_table, B, H_kv, n_new, d, max_blocks_per_seq, num_blocks,
+                      i8 ? 1.f : 1.0f / k_scale, i8 ? 1.f : 1.0f / v_scale, k_scales, v_scales};
+  const long long threads = (long long)B * H_kv * n_new * (d / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (i8) {
+    switch (dtype) {
+      case ATTN_F32: hipLaunchKernelGGL((attn::kv_append_8bit_kernel<attn::F32, true>), grid, dim3(256), 0, st, a); break;
+      case ATTN_F16: hipLaunchKernelGGL((attn::kv_append_8bit_kernel<attn::F16, true>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((attn::kv_append_8bit_kernel<attn::BF16, true>), grid, dim3(256), 0, st, a); break;
+    }
+  } else {
+    switch (dtype) {
+      case ATTN_F32: hipLaunchKernelGGL((attn::kv_append_8bit_kernel<attn::F32, false>), grid, dim3(256), 0, st, a); break;
+      case ATTN_F16: hipLaunchKernelGGL((attn::kv_append_8bit_kernel<attn::F16, false>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((attn::kv_append_8bit_kernel<attn::BF16, false>), grid, dim3(256), 0, st, a); break;
+    }
+  }
+  return launch_status(fn);
+}
+
+}  // namespace
+
+extern "C" {
 
 int kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* cache_lens,
                   const int32_t* block_table, int B, int H_kv, int n_new, int d, int block_size,
                   int max_blocks_per_seq, int num_blocks, int dtype, float k_scale, float v_scale, void* stream) {
-  if (!k_pool || !v_pool || !k_new || !v_new || !cache_lens || !block_table)
-    return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: null pointer");
-  if (B < 1 || H_kv < 1 || n_new < 1) return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: B, H_kv, n_new must be >= 1");
-  if (!valid_dtype(dtype)) return fail(ATTN_ERR_UNSUPPORTED, "kv_append_fp8: dtype %d not supported", dtype);
-  if (!plain_head_dim(d)) return fail(ATTN_ERR_UNSUPPORTED, "kv_append_fp8: head dim %d not supported", d);
-  if (block_size != 16)
-    return fail(ATTN_ERR_UNSUPPORTED, "kv_append_fp8: block_size must be 16 (got %d)", block_size);
-  if (max_blocks_per_seq < 1 || num_blocks < 1)
-    return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: max_blocks_per_seq and num_blocks must be >= 1");
-  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
-    return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: k_scale and v_scale must be finite and positive");
-  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
-    return fail(ATTN_ERR_INVALID_ARG, "kv_append_fp8: tensors must be 16-byte aligned");
-  attn::AppendFp8Args a{static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_new, v_new, cache_lens,
-                        block_table, B, H_kv, n_new, d, max_blocks_per_seq, num_blocks, 1.0f / k_scale,
-                        1.0f / v_scale};
-  const long long threads = (long long)B * H_kv * n_new * (d / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  switch (dtype) {
-    case ATTN_F32: hipLaunchKernelGGL(attn::kv_append_fp8_kernel<attn::F32>, grid, dim3(256), 0, st, a); break;
-    case ATTN_F16: hipLaunchKernelGGL(attn::kv_append_fp8_kernel<attn::F16>, grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(attn::kv_append_fp8_kernel<attn::BF16>, grid, dim3(256), 0, st, a); break;
-  }
-  return launch_status("kv_append_fp8");
+  return append_8bit("kv_append_fp8", false, k_pool, v_pool, k_new, v_new, cache_lens, block_table, B, H_kv, n_new,
+                     d, block_size, max_blocks_per_seq, num_blocks, dtype, k_scale, v_scale, nullptr, nullptr,
+                     stream);
+}
+
+int kv_append_int8(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* cache_lens,
+                   const int32_t* block_table, int B, int H_kv, int n_new, int d, int block_size,
+                   int max_blocks_per_seq, int num_blocks, int dtype, const float* k_scales,
+                   const float* v_scales, void* stream) {
+  return append_8bit("kv_append_int8", true, k_pool, v_pool, k_new, v_new, cache_lens, block_table, B, H_kv, n_new,
+                     d, block_size, max_blocks_per_seq, num_blocks, dtype, 1.f, 1.f, k_scales, v_scales, stream);
 }
 
 int kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n_pairs, int H_kv, int d, int block_size,

@@ -90,7 +90,12 @@ struct DecodeStreamArgs {
   int32_t* piece_cnt;  // [B][H_q]: pieces of segment (b, gh), written by the wave holding piece 0
   int n_hg;            // groups of 16 query heads per KV head
   float v_scale;       // fp8 cache: V = stored value * v_scale (1 otherwise)
+  const float* v_scales;  // int8 cache: [H_kv][d] per-channel scales of V
+  const float* q_fac;     // int8 cache: [B][H_q] factor undoing the query's power-of-two scaling
 };
+
+// Cache element formats of the decode kernel.
+enum DecKV { kKV16 = 0, kKVFp8 = 1, kKVInt8 = 2 };
 
 // Sum over the wave (uniform result).
 __device__ __forceinline__ int wave_sum(int x) {
@@ -119,16 +124,79 @@ __device__ __forceinline__ void fp8x16_to(const u32x4 w, u32x4& lo, u32x4& hi) {
   hi = u32x4{fp8x2_to<T, false>(w[2]), fp8x2_to<T, true>(w[2]), fp8x2_to<T, false>(w[3]), fp8x2_to<T, true>(w[3])};
 }
 
-template <typename T, int D, bool PAGED, bool FP8>
+// Two int8 values (bytes 2 HI, 2 HI + 1 of x, already XORed with 0x80 so that
+// byte u = code + 128) -> two f16 values.  The f16 with bits 0x6400 | u is
+// 1024 + u exactly (spacing 1 in [1024, 2048)); subtracting 1152 leaves the code,
+// exactly (one packed f16 add for the pair).
+template <bool HI>
+__device__ __forceinline__ uint32_t i8x2_to_f16(uint32_t xb) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t y = HI ? (xb >> 16) : xb;
+  const uint32_t w = (y & 0xFFu) | ((y & 0xFF00u) << 8) | 0x64006400u;
+  const h2 r = __builtin_bit_cast(h2, w) - h2{(_Float16)1152.f, (_Float16)1152.f};
+  return __builtin_bit_cast(uint32_t, r);
+}
+// 16 int8 codes (words w[0..3]) -> 16 f16 values in two 16-byte vectors
+__device__ __forceinline__ void i8x16_to_f16(const u32x4 w, u32x4& lo, u32x4& hi) {
+  const u32x4 b = w ^ 0x80808080u;
+  lo = u32x4{i8x2_to_f16<false>(b[0]), i8x2_to_f16<true>(b[0]), i8x2_to_f16<false>(b[1]), i8x2_to_f16<true>(b[1])};
+  hi = u32x4{i8x2_to_f16<false>(b[2]), i8x2_to_f16<true>(b[2]), i8x2_to_f16<false>(b[3]), i8x2_to_f16<true>(b[3])};
+}
+
+// Int8 cache: the key scales fold into the query.  q'[c] = q[c] * s_k[g][c] in
+// fp32; each head's q' is multiplied by 2^(14 - e), with |q'| < 2^e for all its
+// channels, so its largest element lies in [2^13, 2^14) (the logits stay far
+// from overflow), then split into two f16 parts, hi = f16(q') and lo =
+// f16(q' - hi): hi + lo carries about 22 bits, and each part times an integer
+// code is exact in the MFMA's fp32 products.  q16 holds [B][H_q][2][d] (hi row,
+// then lo row); q_fac = 2^(e - 14) undoes the factor in the logit scale.
+// One wave per (head, sequence).
+template <typename T, int D>
+__global__ void __launch_bounds__(64)
+decode_i8_query_kernel(const void* __restrict__ q, const float* __restrict__ k_scales, uint16_t* __restrict__ q16,
+                       float* __restrict__ q_fac, int H_q, int G) {
+  constexpr int E = D / 64;
+  const int h = blockIdx.x, b = blockIdx.y, l = threadIdx.x;
+  const size_t row = ((size_t)b * H_q + h) * D;
+  const float* sk = k_scales + (size_t)(h / G) * D;
+  float v[E];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    v[e] = load_elem<T>(q, row + l + 64 * e) * sk[l + 64 * e];
+    amax = fmaxf(amax, fabsf(v[e]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  // amax < 2^ex (ex from its exponent field), clamped so both powers are normal
+  int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126;
+  ex = ex < -100 ? -100 : (ex > 120 ? 120 : ex);
+  const float up = __uint_as_float((uint32_t)(127 + 14 - ex) << 23);
+  uint16_t* dst = q16 + 2 * row;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float x = v[e] * up;
+    const uint16_t hi = f32_to_f16_bits(x);
+    dst[l + 64 * e] = hi;
+    dst[D + l + 64 * e] = f32_to_f16_bits(x - f16_bits_to_f32(hi));
+  }
+  if (l == 0) q_fac[(size_t)b * H_q + h] = __uint_as_float((uint32_t)(127 - 14 + ex) << 23);
+}
+
+template <typename T, int D, bool PAGED, int KV>
 __global__ void __launch_bounds__(64 * kDecWaves)
 decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const int32_t* __restrict__ table) {
   using Gm = DecGeom<D>;
+  constexpr bool FP8 = KV == kKVFp8, I8 = KV == kKVInt8, Q8 = KV != kKV16;
+  // MFMA operand type: the query's type, except over an int8 cache, where the
+  // codes, the scaled query and P are f16 (codes exact, 11-bit products)
+  using TC = typename std::conditional<I8, F16, T>::type;
   constexpr int KS = D / 32;   // 32-deep k-steps of Q K^T
   constexpr int DB = D / 16;   // 16-wide blocks of d
   constexpr int ROWB = Gm::ROWB, VCH = Gm::VCH;
   // bytes per cache row, and 16-byte pieces of K and of V a lane loads per stage
-  constexpr int RB = FP8 ? D : ROWB;
-  constexpr int NKL = FP8 ? D / 64 : KS, NVL = FP8 ? D / 64 : VCH;
+  constexpr int RB = Q8 ? D : ROWB;
+  constexpr int NKL = Q8 ? D / 64 : KS, NVL = Q8 ? D / 64 : VCH;
 
   __shared__ __attribute__((aligned(1024))) uint8_t vtile[kDecWaves * Gm::SLOT];
 
@@ -218,6 +286,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   const uint8_t* vp = static_cast<const uint8_t*>(a.v);
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const float c_log2 = a.scale_log2;  // > 0 on this path
+  float cl = c_log2;                  // the segment's logit scale (int8: over the rescaled query)
   uint8_t* vt = vtile + w * Gm::SLOT;
 
   // One stage in registers: K rows in MFMA operand layout (lane -> token row
@@ -228,6 +297,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     u32x4 k[NKL];
     u32x4 v[NVL];
     u32x4 q[KS];
+    float qfac;  // int8: the query rows' scaling factor
     bool ok;     // valid block id (paged)
     bool qnew;   // q holds a new segment's query rows
   };
@@ -252,8 +322,8 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     // contiguous: rows past the capacity (last stage only) read the last row instead
     const int kr = PAGED ? col : min(col, a.capacity - 1 - c.st * kDecStage);
     const int vr = PAGED ? (l >> 2) : min(l >> 2, a.capacity - 1 - c.st * kDecStage);
-    if (FP8) {
-      // FP8 rows: lane (col, grp) takes the d-chunks KS grp .. KS grp + KS - 1 of
+    if (Q8) {
+      // 8-bit rows: lane (col, grp) takes the d-chunks KS grp .. KS grp + KS - 1 of
       // its key row (8 KS contiguous bytes); the query fragments use the same
       // assignment of d to k-steps, so the dot products are unchanged.  V: the
       // same rows and columns as the 16-bit layout, a quarter row per lane.
@@ -275,14 +345,17 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     if (S.qnew) {
       // query heads g*G + 16 hg + col (columns past the group repeat head g*G)
       const int gi = 16 * hg + col;
-      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * D + (FP8 ? 8 * KS : 8) * grp;
+      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (I8 ? 2 * D : D) +
+                            (Q8 ? 8 * KS : 8) * grp;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + (FP8 ? 8 : 32) * ks);
+      for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + (Q8 ? 8 : 32) * ks);
+      if constexpr (I8) S.qfac = sa.q_fac[(size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)];
     }
   };
 
   // per-segment state
   u32x4 qf[KS];
+  u32x4 qlo[I8 ? KS : 1];  // int8: the low f16 parts of the scaled query
   f32x4 oacc[DB];
   float m = kNegInf, lsum = 0.f, lexact = 0.f;
   int piece = 0;
@@ -302,8 +375,11 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       const size_t pidx = ((size_t)c.b * a.H_q + g * G + gi) * a.s_max + piece;
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = oacc[db] * (FP8 ? inv * sa.v_scale : inv);
+      for (int db = 0; db < DB; ++db) {
+        f32x4 o = oacc[db] * (FP8 ? inv * sa.v_scale : inv);
+        if constexpr (I8) o *= *reinterpret_cast<const f32x4*>(sa.v_scales + (size_t)g * D + 16 * db + 4 * grp);
+        *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = o;
+      }
       if (grp == 0) a.part_lse[pidx] = e_tot > 0.f ? (m + __log2f(e_tot)) * kLn2 : kNegInf;
     }
   };
@@ -315,6 +391,16 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       // that sees a finite score rescales it by exp2(-inf) = 0.
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = S.q[ks];
+      if constexpr (I8) {
+        cl = c_log2 * S.qfac;
+        // the low parts, loaded here (segment starts are rare): the wait also
+        // covers the next stage's loads, which were issued before this stage's compute
+        const int g = c.gh / sa.n_hg, gi = 16 * (c.gh % sa.n_hg) + col;
+        const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (2 * D) + D + 8 * KS * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qlo[ks] = *reinterpret_cast<const u32x4*>(src + 8 * ks);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
       m = kNegInf;
       lsum = 0.f;
       lexact = 0.f;
@@ -334,20 +420,28 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     };
     const int t0 = c.st * kDecStage;
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (FP8) {
+    if constexpr (Q8) {
+      auto widen = [&](const u32x4 w, u32x4& lo, u32x4& hi) {
+        if constexpr (I8) i8x16_to_f16(w, lo, hi);
+        else fp8x16_to<T>(w, lo, hi);
+      };
 #pragma unroll
       for (int i = 0; i < NVL; ++i) {
         u32x4 lo, hi;
-        fp8x16_to<T>(S.v[i], lo, hi);
+        widen(S.v[i], lo, hi);
         put_v(2 * i, lo);
         put_v(2 * i + 1, hi);
       }
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
         u32x4 lo, hi;
-        fp8x16_to<T>(S.k[i], lo, hi);
-        sacc = mfma16k32<T>(lo, qf[2 * i], sacc);
-        sacc = mfma16k32<T>(hi, qf[2 * i + 1], sacc);
+        widen(S.k[i], lo, hi);
+        sacc = mfma16k32<TC>(lo, qf[2 * i], sacc);
+        sacc = mfma16k32<TC>(hi, qf[2 * i + 1], sacc);
+        if constexpr (I8) {
+          sacc = mfma16k32<TC>(lo, qlo[2 * i], sacc);
+          sacc = mfma16k32<TC>(hi, qlo[2 * i + 1], sacc);
+        }
       }
     } else {
 #pragma unroll
@@ -363,7 +457,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     tmax = fmaxf(tmax, xor_shfl(tmax, 16));
     tmax = max_pair32(tmax);
-    const float mt = tmax * c_log2;
+    const float mt = tmax * cl;
     const bool raise = mt > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float m_new = raise ? mt : m;
@@ -377,9 +471,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     const float base = m == kNegInf ? 0.f : m;
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sacc[i], c_log2, -base));
-    const u32x2 pf = u32x2{cvt_pk<T>(p[0], p[1]), cvt_pk<T>(p[2], p[3])};
-    lsum = add_pair<T>(pf[1], add_pair<T>(pf[0], lsum));
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sacc[i], cl, -base));
+    const u32x2 pf = u32x2{cvt_pk<TC>(p[0], p[1]), cvt_pk<TC>(p[2], p[3])};
+    lsum = add_pair<TC>(pf[1], add_pair<TC>(pf[0], lsum));
     lexact += (p[0] + p[1]) + (p[2] + p[3]);
     // O^T += V^T P^T (the wave's own LDS writes above precede these reads)
 #pragma unroll
@@ -387,7 +481,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       const int ch = ((16 * db + 4 * vq) >> 3) ^ Gm::swz_v(vrow);
       const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4*)(vt + vrow * ROWB + 16 * ch + 2 * ((4 * vq) & 7)));
-      oacc[db] = mfma16k16<T>(vf, pf, oacc[db]);
+      oacc[db] = mfma16k16<TC>(vf, pf, oacc[db]);
     }
     if (c.st + 1 == c.n || last) finish(c);
   };

@@ -114,7 +114,18 @@ __device__ __forceinline__ float in_to_f32<F16>(const void* p, int64_t i) {
   return (float)static_cast<const _Float16*>(p)[i];
 }
 
-struct AppendFp8Args {
+// int8 cache with one scale per (KV head, channel): a few keys are very large,
+// so one scale for a whole tensor would magnify their error ("KV Cache:推理慢的
+// 真正原因", 工程优化手段, the quantization item).  code = rint(x / s[h][c]) in
+// fp32 (the quotient correctly rounded, rint ties to even), clamped to
+// [-127, 127]; NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_i8(float x, float s) {
+  float r = __builtin_rintf(x / s);
+  r = r != r ? 0.f : fminf(fmaxf(r, -127.f), 127.f);
+  return (uint32_t)(int32_t)r & 0xFFu;
+}
+
+struct Append8Args {
   uint8_t* k_pool;
   uint8_t* v_pool;
   const void* k_new;
@@ -123,12 +134,15 @@ struct AppendFp8Args {
   const int32_t* block_table;
   int B, H_kv, n_new, d;
   int max_blocks_per_seq, num_blocks;
-  float k_inv, v_inv;  // 1 / scale, in fp32
+  float k_inv, v_inv;                  // FP8: 1 / scale, in fp32
+  const float* k_scales;               // int8: [H_kv][d]
+  const float* v_scales;
 };
 
-// One thread quantizes 8 consecutive elements of a K row and of the V row.
-template <typename TIN>
-__global__ void __launch_bounds__(256) kv_append_fp8_kernel(AppendFp8Args a) {
+// One thread quantizes 8 consecutive elements of a K row and of the V row,
+// to FP8 E4M3 (I8 = false) or to int8 with per-channel scales (I8 = true).
+template <typename TIN, bool I8>
+__global__ void __launch_bounds__(256) kv_append_8bit_kernel(Append8Args a) {
   const int per_row = a.d / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.B * a.H_kv * a.n_new * per_row;
@@ -157,10 +171,20 @@ __global__ void __launch_bounds__(256) kv_append_fp8_kernel(AppendFp8Args a) {
   const int64_t dst = (((int64_t)blk * a.H_kv + h) * 16 + (p & 15)) * a.d + 8 * c;
   const int64_t src = row * a.d + 8 * c;
   uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+  if constexpr (I8) {
+    const float* ksc = a.k_scales + (int64_t)h * a.d + 8 * c;
+    const float* vsc = a.v_scales + (int64_t)h * a.d + 8 * c;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    kw[e >> 2] |= f32_to_e4m3(in_to_f32<TIN>(a.k_new, src + e) * a.k_inv) << (8 * (e & 3));
-    vw[e >> 2] |= f32_to_e4m3(in_to_f32<TIN>(a.v_new, src + e) * a.v_inv) << (8 * (e & 3));
+    for (int e = 0; e < 8; ++e) {
+      kw[e >> 2] |= f32_to_i8(in_to_f32<TIN>(a.k_new, src + e), ksc[e]) << (8 * (e & 3));
+      vw[e >> 2] |= f32_to_i8(in_to_f32<TIN>(a.v_new, src + e), vsc[e]) << (8 * (e & 3));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kw[e >> 2] |= f32_to_e4m3(in_to_f32<TIN>(a.k_new, src + e) * a.k_inv) << (8 * (e & 3));
+      vw[e >> 2] |= f32_to_e4m3(in_to_f32<TIN>(a.v_new, src + e) * a.v_inv) << (8 * (e & 3));
+    }
   }
   *reinterpret_cast<uint2*>(a.k_pool + dst) = make_uint2(kw[0], kw[1]);
   *reinterpret_cast<uint2*>(a.v_pool + dst) = make_uint2(vw[0], vw[1]);

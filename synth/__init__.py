@@ -330,8 +330,8 @@ def int8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
     ``SFC64(case.seed + 8000)``, in this order:
 
     * ``k_scales``, ``v_scales`` [H_kv, d] float32: 2^u with u uniform in
-      [-7, -4], and in every KV head 4 random channels of K multiplied by 16
-      (outlier key channels);
+      [-9, -6) (values up to 2), and in every KV head 4 random channels of K
+      multiplied by 8 (outlier key channels, values up to 16);
     * the pools' codes: K's whole pool then V's, uniform integers in
       [-127, 127] where a slot holds a cached token; slots holding none carry
       K = 0 and V = 127 (the largest code).
@@ -341,10 +341,10 @@ def int8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
     table = out["block_table"]
     nblk, Hk, bs, d = out["k_pool"].shape
     rng = make_rng(case.seed + 8000)
-    ks = np.exp2(rng.uniform(-7.0, -4.0, size=(Hk, d))).astype(np.float32)
+    ks = np.exp2(rng.uniform(-9.0, -6.0, size=(Hk, d))).astype(np.float32)
     for h in range(Hk):
-        ks[h, rng.choice(d, size=4, replace=False)] *= np.float32(16.0)
-    vs = np.exp2(rng.uniform(-7.0, -4.0, size=(Hk, d))).astype(np.float32)
+        ks[h, rng.choice(d, size=4, replace=False)] *= np.float32(8.0)
+    vs = np.exp2(rng.uniform(-9.0, -6.0, size=(Hk, d))).astype(np.float32)
     held = np.zeros((nblk, bs), dtype=bool)
     for b in range(case.B):
         L = int(lens[b])
