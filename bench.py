@@ -12,7 +12,9 @@ One step runs every stage of the path once, each on its own workload:
                (chunked prefill against the paged cache), bf16, B=16, H_q=32,
                H_kv=8, d=128, cached prefixes uniform in [0, 4096];
   * fp8      : kv_append_fp8 + attn_decode_paged_fp8, the paged workload with
-               the cache stored as OCP FP8 E4M3 (KV GB/s counts 1-byte values).
+               the cache stored as OCP FP8 E4M3 (KV GB/s counts 1-byte values);
+  * int8     : kv_append_int8 + attn_decode_paged_int8, the same with an int8
+               cache and per-channel scales.
 Inputs are seeded synthetic tensors already resident in HBM.  Each kernel call
 is bracketed by HIP events on the stream it runs on.
 
@@ -234,11 +236,19 @@ def main() -> int:
     f_out = torch.empty_like(g["q"])
     f_bytes = int(np.sum((finp["lens"] + fcase.n_new).astype(np.int64))) * fcase.H_kv * fcase.d * 2  # 1 byte each
     del finp
+    # ... and over an int8 cache with per-channel scales
+    iinp = synth.int8_decode_inputs(gcase, base=ginp)
+    i_kp = torch.from_numpy(iinp["k_pool"]).cuda()
+    i_vp = torch.from_numpy(iinp["v_pool"]).cuda()
+    i_ks = torch.from_numpy(iinp["k_scales"]).cuda()
+    i_vs = torch.from_numpy(iinp["v_scales"]).cuda()
+    i_out = torch.empty_like(g["q"])
+    del iinp
     log(f"fp8 decode inputs ready ({time.perf_counter() - t_gen:.1f} s)")
     torch.cuda.synchronize()
 
     legs = ["prefill", "paged_append", "paged_decode", "contig_append", "contig_decode", "chunk_append",
-            "chunk_prefill", "fp8_append", "fp8_decode"]
+            "chunk_prefill", "fp8_append", "fp8_decode", "int8_append", "int8_decode"]
 
     def step(ev=None):
         def rec(i):
@@ -267,6 +277,11 @@ def main() -> int:
         K.attn_decode_paged_fp8(g["q"], f_kp, f_vp, g_table, g_seq, k_scale=0.5, v_scale=0.5,
                                 scale=fcase.sm_scale, workspace=g_ws, out=f_out)
         rec(9)
+        K.kv_append_int8(i_kp, i_vp, g["k_new"], g["v_new"], g_lens, g_table, i_ks, i_vs)
+        rec(10)
+        K.attn_decode_paged_int8(g["q"], i_kp, i_vp, g_table, g_seq, i_ks, i_vs, scale=fcase.sm_scale,
+                                 workspace=g_ws, out=i_out)
+        rec(11)
 
     if args.calibrate_copy:
         # torch's elementwise multiply: reads 2^30 bytes, writes 2^30 bytes per launch
@@ -306,6 +321,7 @@ def main() -> int:
     c_gbs = c_bytes / (ms["contig_decode"] * 1e-3) / 1e9
     k_tflops = k_flops / (ms["chunk_prefill"] * 1e-3) / 1e12
     f_gbs = f_bytes / (ms["fp8_decode"] * 1e-3) / 1e9
+    i_gbs = f_bytes / (ms["int8_decode"] * 1e-3) / 1e9  # same 1-byte cache
 
     def roof(bound, achieved, peak, unit, kernel, per_unit):
         return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -357,6 +373,14 @@ def main() -> int:
             "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["fp8_decode"], 3),
             "roofline": roof("hbm", f_gbs, PEAK_HBM_GBS, "GB/s", "decode_mfma_kernel<BF16,128,paged,fp8>+merge",
                              {"bytes": f_bytes}),
+        },
+        "decode_paged_int8": {
+            "value": round(i_gbs, 1), "unit": "GB/s", "workload": fcase.name + " (int8 cache, per-channel scales)",
+            "kv_bytes": f_bytes, "ms_mean": round(ms["int8_decode"], 4), "ms_median": round(med["int8_decode"], 4),
+            "append_ms": round(ms["int8_append"], 4),
+            "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["int8_decode"], 3),
+            "roofline": roof("hbm", i_gbs, PEAK_HBM_GBS, "GB/s",
+                             "decode_i8_query+decode_mfma_kernel<BF16,128,paged,int8>+merge", {"bytes": f_bytes}),
         },
         "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
         "device_error_flags": flags,
