@@ -33,7 +33,7 @@ from .attention import (one_shot, softmax_weights, tiled, splitk_merge, attentio
 from .brute import brute_attention
 from .caches import ListCache, ContigCache, PagedCache
 from .decode import cached_decode, naive_decode, decode_step, chunk_step
-from .fp8 import E4M3_VALUES, e4m3_round, e4m3_value, quantize, decode_step_fp8
+from .fp8 import E4M3_VALUES, e4m3_round, e4m3_value, quantize, decode_step_fp8, prefill_fp8
 from .block_pool import FreeListPool, NoBlocks, blocks_for, simulate
 from .int8 import quantize_int8, dequantize_int8, decode_step_int8
 
@@ -43,7 +43,7 @@ __all__ = [
     "brute_attention",
     "ListCache", "ContigCache", "PagedCache",
     "cached_decode", "naive_decode", "decode_step", "chunk_step",
-    "E4M3_VALUES", "e4m3_round", "e4m3_value", "quantize", "decode_step_fp8",
+    "E4M3_VALUES", "e4m3_round", "e4m3_value", "quantize", "decode_step_fp8", "prefill_fp8",
     "FreeListPool", "NoBlocks", "blocks_for", "simulate",
     "quantize_int8", "dequantize_int8", "decode_step_int8",
 ]

@@ -14,9 +14,17 @@ m * 2^-9; no infinities; 0x7F / 0xFF are NaN; the largest finite value is
             ties to the even code (mantissa LSB 0), |.| >= 448 -> +-448, NaN -> NaN
     value = E4M3(code) * scale
 
+FP8 prefill (the FP8 attention of FlashAttention-3 named in "KV缓存与Flash注意力",
+版本演进 table and Flash Attention section): Q, K and V are E4M3 codes with one
+scale each; the result is attention over the dequantized values,
+
+    O = softmax(scale * (q_scale Q) (k_scale K)^T) (v_scale V).
+
 Pins (tests/test_oracle_fp8.py): the format's landmark values, brute-force
-nearest-value rounding on random and tie inputs, code round trips, and a decode
-step equal to attention over the dequantized cache.
+nearest-value rounding on random and tie inputs, code round trips, a decode
+step equal to attention over the dequantized cache, and FP8 prefill equal to
+one-shot attention over dequantized values computed apart, with the scales
+entering as stated.
 """
 from __future__ import annotations
 
@@ -100,3 +108,17 @@ def decode_step_fp8(cache: PagedCache, q: np.ndarray, k_new: np.ndarray, v_new: 
         for r, h in enumerate(hs):
             O[b, h], L[b, h] = o[r], ls[r]
     return O, L
+
+
+def prefill_fp8(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_scale: float, k_scale: float, v_scale: float,
+                scale: float, causal: bool, rows=None):
+    """Attention over E4M3 codes q [B, H_q, N, d], k, v [B, H_kv, N, d] (uint8),
+    each dequantized as code value * its scale.  Returns (O, lse) in fp64, for
+    all rows or for the (b, h, i) triples in ``rows`` (as ``attention_rows``)."""
+    Q = e4m3_value(q) * np.float64(q_scale)
+    K = e4m3_value(k) * np.float64(k_scale)
+    V = e4m3_value(v) * np.float64(v_scale)
+    if rows is None:
+        from .attention import one_shot
+        return one_shot(Q, K, V, scale, causal=causal)
+    return attention_rows(Q, K, V, scale, rows, causal=causal)

@@ -77,3 +77,37 @@ def test_fp8_decode_step_is_attention_over_dequantized_values():
         assert np.max(np.abs(O[b] - Oo[0, :, 0])) <= 1e-12 and np.max(np.abs(L[b] - Lo[0, :, 0])) <= 1e-12
         # the new token's codes are the quantized new rows
         assert np.array_equal(Kc[:, -1], oracle.quantize(inp["k_new"][b, :, 0], "bf16", 0.5))
+
+
+def _e4m3_by_formula(c):
+    """Value of one E4M3 code from its bit fields (independent of the table)."""
+    c = int(c)
+    s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+    mag = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+def test_fp8_prefill_is_brute_force_attention_over_dequantized_values():
+    case = synth.PrefillCase("f8p", 1, 4, 2, 9, 8, "bf16", True, True, 41)
+    inp = synth.fp8_prefill_inputs(case)
+    qs, ks, vs, scale = 0.5, 0.25, 2.0, 0.3
+    O, L = oracle.prefill_fp8(inp["q"], inp["k"], inp["v"], qs, ks, vs, scale, causal=True)
+    deq = np.vectorize(_e4m3_by_formula)
+    Q, K, V = deq(inp["q"]) * qs, deq(inp["k"]) * ks, deq(inp["v"]) * vs
+    Ob, Lb = oracle.brute_attention(Q, K, V, scale, causal=True)
+    assert np.max(np.abs(O - Ob)) <= 1e-12 and np.max(np.abs(L - Lb)) <= 1e-12
+
+
+def test_fp8_prefill_scales_enter_as_stated():
+    case = synth.PrefillCase("f8p", 1, 2, 1, 33, 16, "bf16", False, True, 42)
+    inp = synth.fp8_prefill_inputs(case)
+    O1, L1 = oracle.prefill_fp8(inp["q"], inp["k"], inp["v"], 1.0, 1.0, 1.0, 0.25, causal=False)
+    # q_scale and k_scale multiply the logits like scale does; v_scale scales O and leaves lse
+    O2, L2 = oracle.prefill_fp8(inp["q"], inp["k"], inp["v"], 2.0, 0.5, 4.0, 0.25, causal=False)
+    O3, L3 = oracle.prefill_fp8(inp["q"], inp["k"], inp["v"], 2.0, 1.0, 1.0, 0.125, causal=False)
+    assert np.allclose(O2, 4.0 * O1, atol=1e-12) and np.allclose(L2, L1, atol=1e-12)
+    assert np.allclose(O3, O1, atol=1e-12) and np.allclose(L3, L1, atol=1e-12)
+    rows = [(0, 1, 0), (0, 0, 32), (0, 1, 17)]
+    Or, Lr = oracle.prefill_fp8(inp["q"], inp["k"], inp["v"], 1.0, 1.0, 1.0, 0.25, causal=False, rows=rows)
+    for r, (b, h, i) in enumerate(rows):
+        assert np.allclose(Or[r], O1[b, h, i], atol=1e-12) and abs(Lr[r] - L1[b, h, i]) <= 1e-12
