@@ -191,6 +191,31 @@ int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
                        int dtype, void* stream);
 
 /*
+ * attn_prefill_fp8 -- attn_prefill over FP8 E4M3 inputs.
+ *
+ * The FP8 attention of FlashAttention-3 ("KV缓存与Flash注意力", the 版本演进
+ * table and the Flash Attention section): q [B, H_q, N, d] and k, v
+ * [B, H_kv, N, d] are E4M3 codes (one byte each, the format of kv_append_fp8),
+ * with one fp32 scale per tensor; the result is attention over the
+ * dequantized values:
+ *   O = softmax(scale * (q_scale Q)(k_scale K)^T) (v_scale V)
+ * o [B, H_q, N, d] in out_dtype (F16 or BF16); lse as for attn_prefill.
+ * Q K^T runs on the FP8 matrix cores (exact products, fp32 sums).  V's codes
+ * are first widened (exactly) into `workspace` as out_dtype values, and P V
+ * runs as in the 16-bit kernel, P rounded to out_dtype.
+ * workspace: device, attn_prefill_fp8_workspace_bytes(B, H_kv, N, d) bytes.
+ * Errors: INVALID_ARG (pointers, sizes, scales, alignment), UNSUPPORTED
+ *         (out_dtype, d not 64 / 128, scale <= 0), WORKSPACE, HIP.
+ */
+int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H_q, int H_kv, int N, int d, int causal, float scale,
+                     float q_scale, float k_scale, float v_scale, int out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of attn_prefill_fp8: 2 * B * H_kv * N * d (0 on invalid sizes). */
+size_t attn_prefill_fp8_workspace_bytes(int B, int H_kv, int N, int d);
+
+/*
  * kv_append_fp8 / attn_decode_paged_fp8 -- a paged KV cache stored in 8 bits.
  *
  * Storing the cache in 8 bits halves the bytes decode must read ("KV Cache:

@@ -25,7 +25,7 @@ import torch
 __all__ = [
     "AttnError", "lib", "lib_path", "attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode",
     "attn_decode_paged", "kv_append_fp8", "attn_decode_paged_fp8", "kv_append_int8", "attn_decode_paged_int8",
-    "kv_copy_blocks",
+    "kv_copy_blocks", "attn_prefill_fp8", "attn_prefill_fp8_workspace_bytes",
     "attn_decode_workspace_bytes", "attn_device_error_flags", "attn_version", "DTYPE_CODES",
     "EXPORTED_SYMBOLS",
 ]
@@ -39,7 +39,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3:
           4: "ATTN_ERR_HIP", 5: "ATTN_ERR_NO_BLOCKS"}
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
                     "kv_append_fp8", "attn_decode_paged_fp8", "kv_append_int8", "attn_decode_paged_int8",
-                    "kv_copy_blocks",
+                    "kv_copy_blocks", "attn_prefill_fp8", "attn_prefill_fp8_workspace_bytes",
                     "attn_decode_workspace_bytes", "attn_last_error", "attn_version",
                     "attn_device_error_flags",
                     "attn_block_pool_create", "attn_block_pool_destroy", "attn_block_pool_free_blocks",
@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.attn_version.restype = ctypes.c_char_p
     L.attn_device_error_flags.argtypes = [vp]
     L.kv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.attn_prefill_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, f32, f32, i32, vp, sz,
+                                   vp]
+    L.attn_prefill_fp8_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.attn_prefill_fp8_workspace_bytes.restype = sz
     L.kv_append_int8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     L.attn_decode_paged_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp,
                                          vp, i32, vp, sz, vp]
@@ -97,7 +101,7 @@ def lib() -> ctypes.CDLL:
     L.attn_block_pool_fork.argtypes = [vp, vp, vp, i32, i32]
     for name in ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
                  "kv_append_fp8", "attn_decode_paged_fp8", "attn_device_error_flags", "kv_copy_blocks",
-                 "kv_append_int8", "attn_decode_paged_int8",
+                 "kv_append_int8", "attn_decode_paged_int8", "attn_prefill_fp8",
                  "attn_block_pool_free_blocks", "attn_block_pool_holders", "attn_block_pool_reserve",
                  "attn_block_pool_reserve_batch", "attn_block_pool_release", "attn_block_pool_fork"):
         getattr(L, name).restype = i32
@@ -377,4 +381,37 @@ def attn_decode_paged_int8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
                                       _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                       _stream())
     _check("attn_decode_paged_int8", rc)
+    return (out, lse) if return_lse else out
+
+
+def attn_prefill_fp8_workspace_bytes(B: int, H_kv: int, N: int, d: int) -> int:
+    return int(lib().attn_prefill_fp8_workspace_bytes(B, H_kv, N, d))
+
+
+def attn_prefill_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                     scale: Optional[float] = None, q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0,
+                     out_dtype=torch.bfloat16, return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Attention over FP8 E4M3 codes (uint8) q [B, H_q, N, d], k, v [B, H_kv, N, d],
+    each times its scale; the output in out_dtype (torch.bfloat16 or torch.float16)."""
+    B, H_q, N, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, N, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_kv, N, d] matching q")
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8 or v.dtype != torch.uint8:
+        raise ValueError("FP8 inputs are uint8 tensors of E4M3 codes")
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float16")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = attn_prefill_fp8_workspace_bytes(B, H_kv, N, d)
+    workspace = _workspace(workspace, nbytes, q.device)
+    out = torch.empty((B, H_q, N, d), dtype=out_dtype, device=q.device) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device)
+    rc = lib().attn_prefill_fp8(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out", out_dtype),
+                                _dev(lse, "lse", torch.float32) if return_lse else 0, B, H_q, H_kv, N, d,
+                                int(bool(causal)), scale, float(q_scale), float(k_scale), float(v_scale),
+                                DTYPE_CODES[out_dtype], _dev(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream())
+    _check("attn_prefill_fp8", rc)
     return (out, lse) if return_lse else out

@@ -122,7 +122,7 @@ int prefill_plain_d(const attn::PrefillArgs& a, int d, bool causal, hipStream_t 
   return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not supported", d);
 }
 
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, bool F8 = false>
 int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st, const attn::PagedKV& pk = {0, 0},
                         const int32_t* table = nullptr, const int32_t* cache_lens = nullptr) {
   constexpr int NW = attn::kPrefillWaves;
@@ -132,16 +132,16 @@ int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st,
   const dim3 grid((unsigned)blocks), block(64 * NW);
   const bool lse = a.lse != nullptr;
   if (causal && lse)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, true, PAGED>), grid, block, 0, st, a, pk, table,
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, true, PAGED, F8>), grid, block, 0, st, a, pk, table,
                        cache_lens);
   else if (causal)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, false, PAGED>), grid, block, 0, st, a, pk, table,
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, true, false, PAGED, F8>), grid, block, 0, st, a, pk, table,
                        cache_lens);
   else if (lse)
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, true, PAGED>), grid, block, 0, st, a, pk, table,
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, true, PAGED, F8>), grid, block, 0, st, a, pk, table,
                        cache_lens);
   else
-    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, false, PAGED>), grid, block, 0, st, a, pk, table,
+    hipLaunchKernelGGL((attn::prefill_mfma_kernel<T, D, NW, false, false, PAGED, F8>), grid, block, 0, st, a, pk, table,
                        cache_lens);
   return launch_status("attn_prefill");
 }
@@ -149,6 +149,20 @@ int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st,
 template <typename T>
 int prefill_mfma_d(const attn::PrefillArgs& a, int d, bool causal, hipStream_t st) {
   return d == 64 ? launch_prefill_mfma<T, 64, false>(a, causal, st) : launch_prefill_mfma<T, 128, false>(a, causal, st);
+}
+
+// FP8 prefill: V's codes widened to T in the workspace, then the kernel with
+// FP8 Q K^T.
+template <typename T>
+int prefill_fp8_d(attn::PrefillArgs a, int d, bool causal, void* vwide, hipStream_t st) {
+  const size_t n16 = (size_t)a.B * a.H_kv * a.N * d / 16;
+  hipLaunchKernelGGL((attn::fp8_widen_kernel<T>), dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const attn::u32x4*>(a.v), static_cast<attn::u32x4*>(vwide), n16);
+  const int rc = launch_status("attn_prefill_fp8 widen");
+  if (rc != ATTN_OK) return rc;
+  a.v = vwide;
+  return d == 64 ? launch_prefill_mfma<T, 64, false, true>(a, causal, st)
+                 : launch_prefill_mfma<T, 128, false, true>(a, causal, st);
 }
 
 template <typename T>
@@ -315,6 +329,39 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
     case ATTN_F16: return prefill_plain_d<attn::F16>(a, d, c, st);
     default: return prefill_plain_d<attn::BF16>(a, d, c, st);
   }
+}
+
+size_t attn_prefill_fp8_workspace_bytes(int B, int H_kv, int N, int d) {
+  if (B < 1 || H_kv < 1 || N < 1 || d < 1) return 0;
+  return (size_t)B * H_kv * N * d * 2;
+}
+
+int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H_q, int H_kv, int N,
+                     int d, int causal, float scale, float q_scale, float k_scale, float v_scale, int out_dtype,
+                     void* workspace, size_t workspace_bytes_given, void* stream) {
+  const char* fn = "attn_prefill_fp8";
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (B < 1 || H_q < 1 || H_kv < 1 || N < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: B, H_q, H_kv, N must be >= 1", fn);
+  if (H_q % H_kv != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "%s: H_q (%d) is not a multiple of H_kv (%d)", fn, H_q, H_kv);
+  if (B > 65535 || H_q > 65535) return fail(ATTN_ERR_INVALID_ARG, "%s: B or H_q too large", fn);
+  if (!(out_dtype == ATTN_F16 || out_dtype == ATTN_BF16) || !(d == 64 || d == 128))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: f16/bf16 output with d = 64 or 128 only", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_UNSUPPORTED, "%s: scale must be positive", fn);
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale) || !(q_scale > 0.f) ||
+      !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(ATTN_ERR_INVALID_ARG, "%s: q_scale, k_scale and v_scale must be finite and positive", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(ATTN_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  if ((long long)N * d > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "%s: N*d too large", fn);
+  const size_t need = attn_prefill_fp8_workspace_bytes(B, H_kv, N, d);
+  if (!workspace || workspace_bytes_given < need)
+    return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes_given);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  attn::PrefillArgs a{q, k, v, o, lse, B, H_q, H_kv, N, scale * q_scale * k_scale * attn::kLog2e, 0, v_scale};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return out_dtype == ATTN_BF16 ? prefill_fp8_d<attn::BF16>(a, d, causal != 0, workspace, st)
+                                : prefill_fp8_d<attn::F16>(a, d, causal != 0, workspace, st);
 }
 
 int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,

@@ -124,6 +124,19 @@ __device__ __forceinline__ void fp8x16_to(const u32x4 w, u32x4& lo, u32x4& hi) {
   hi = u32x4{fp8x2_to<T, false>(w[2]), fp8x2_to<T, true>(w[2]), fp8x2_to<T, false>(w[3]), fp8x2_to<T, true>(w[3])};
 }
 
+// FP8 E4M3 codes -> the same values in T (exact), 16 per thread; used to hand
+// V to the 16-bit P V of the FP8 prefill.
+template <typename T>
+__global__ void __launch_bounds__(256) fp8_widen_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        size_t n16) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  u32x4 lo, hi;
+  fp8x16_to<T>(src[i], lo, hi);
+  dst[2 * i] = lo;
+  dst[2 * i + 1] = hi;
+}
+
 // Two int8 values (bytes 2 HI, 2 HI + 1 of x, already XORed with 0x80 so that
 // byte u = code + 128) -> two f16 values.  The f16 with bits 0x6400 | u is
 // 1024 + u exactly (spacing 1 in [1024, 2048)); subtracting 1152 leaves the code,

@@ -57,6 +57,15 @@ __device__ __forceinline__ f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// FP8 E4M3 x E4M3 -> fp32, 32 x 32 output, 64-deep (gfx950); 32 bytes of A
+// (one row of K) and of B (one column of Q^T) per lane.  Unit block scales
+// (E8M0 127 = 2^0): the tensor scales are applied outside.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32_fp8(u32x4 a0, u32x4 a1, i32x8 b, f32x16 c) {
+  const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 constexpr int kPrefillWaves = 4;  // waves (of 32 query rows) per prefill workgroup
 
@@ -153,7 +162,10 @@ struct PagedKV {
 // from the table directly.
 constexpr int kLdsBlocks = 2048;
 
-template <typename T, int D, int NW, bool CAUSAL, bool LSE, bool PAGED>
+// F8: Q and K are FP8 E4M3 codes (one byte per element) and Q K^T runs on the
+// FP8 matrix cores; V arrives as 16-bit values of T (the codes, widened
+// exactly by the caller) and P V runs in T as in the 16-bit kernel.
+template <typename T, int D, int NW, bool CAUSAL, bool LSE, bool PAGED, bool F8 = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table,
                     const int32_t* __restrict__ cache_lens) {
@@ -162,6 +174,11 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
   constexpr int KS = D / 16;  // 16-deep k-steps of Q K^T
   constexpr int DB = D / 32;  // 32-wide blocks of the output's d
   static_assert(Gm::COPIES >= 1, "tile shape");
+  static_assert(!(F8 && PAGED), "FP8 inputs are contiguous");
+  // K tile geometry: an FP8 row of D bytes has the size of D / 2 16-bit elements
+  using GK = PrefillGeom<F8 ? D / 2 : D, NW>;
+  constexpr int KROWB = GK::ROWB;
+  constexpr int K8S = D / 64;  // 64-deep k-steps of the FP8 Q K^T
 
   // [buffer][K, V] tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][TILE];
@@ -236,6 +253,8 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
   // lane offset; the ragged last tile clamps each row to the last key.
   const int r0 = w * Gm::ROWS_PER_COPY + l / CH;  // row of copy 0
   const uint32_t koff = r0 * ROWB + 16 * ((l % CH) ^ Gm::swz_k(r0));
+  const int r0k = w * GK::ROWS_PER_COPY + l / GK::CH;  // FP8 K: row of copy 0
+  const uint32_t koff8 = r0k * KROWB + 16 * ((l % GK::CH) ^ GK::swz_k(r0k));
   const uint32_t voff = r0 * ROWB + 16 * ((l % CH) ^ Gm::swz_v(r0));
   constexpr int kCopyStride = NW * 1024;  // bytes between consecutive copies of a wave
   // one tensor's tile: src = K or V, off = its lane offset, which = 0 (K) / 1 (V)
@@ -315,7 +334,25 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
       }
     }
   };
-  auto issue_k = [&](int k0, int buf) { issue(kp, koff, 0, k0, buf); };
+  auto issue_k = [&](int k0, int buf) {
+    if constexpr (F8) {
+      const uint32_t dst = smem_base + 2 * buf * TILE + w * 1024;
+      const uint8_t* tile_base = static_cast<const uint8_t*>(a.k) + kv_base + (size_t)k0 * D;
+      if (k0 + BN <= a.N) {
+#pragma unroll
+        for (int i = 0; i < GK::COPIES; ++i) lds_copy16(tile_base + i * kCopyStride, koff8, dst + i * kCopyStride);
+      } else {
+#pragma unroll
+        for (int i = 0; i < GK::COPIES; ++i) {
+          const int r = r0k + i * NW * GK::ROWS_PER_COPY;
+          const ptrdiff_t shift = (ptrdiff_t)(min(k0 + r, a.N - 1) - (k0 + r)) * KROWB;  // <= 0
+          lds_copy16(tile_base + i * kCopyStride + koff8 + shift, dst + i * kCopyStride);
+        }
+      }
+    } else {
+      issue(kp, koff, 0, k0, buf);
+    }
+  };
   auto issue_v = [&](int k0, int buf) { issue(vp, voff, 1, k0, buf); };
   auto issue_v_full = [&](int k0, int buf) {  // a tile known to lie inside the sequence
     if (PAGED) {
@@ -329,13 +366,29 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
   };
 
   // Q^T fragments (B operand): lane -> query qi, k-slots -> d = 16 ks + 8 hh + j
-  u32x4 qf[KS];
+  // (F8: 32 bytes per 64-deep step, d = 64 ks + 32 hh + j; K rows use the same
+  // assignment, so the products pair the same d whatever order the matrix
+  // core gives the 32 bytes)
+  u32x4 qf[F8 ? 1 : KS];
+  i32x8 qf8[F8 ? K8S : 1];
   {
     const bool ok = qi < a.N;
-    const uint16_t* src = qp + (((size_t)b * a.H_q + h) * a.N + (ok ? qi : 0)) * D + 8 * hh;
+    const size_t qrow = (((size_t)b * a.H_q + h) * a.N + (ok ? qi : 0)) * D;
+    if constexpr (F8) {
+      const uint8_t* src = static_cast<const uint8_t*>(a.q) + qrow + 32 * hh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = ok ? *reinterpret_cast<const u32x4*>(src + 16 * ks) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < K8S; ++ks) {
+        const u32x4 x0 = ok ? *reinterpret_cast<const u32x4*>(src + 64 * ks) : u32x4{0, 0, 0, 0};
+        const u32x4 x1 = ok ? *reinterpret_cast<const u32x4*>(src + 64 * ks + 16) : u32x4{0, 0, 0, 0};
+        qf8[ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2],
+                        (int)x1[3]};
+      }
+    } else {
+      const uint16_t* src = qp + qrow + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = ok ? *reinterpret_cast<const u32x4*>(src + 16 * ks) : u32x4{0, 0, 0, 0};
+      }
     }
   }
 
@@ -353,6 +406,20 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
     const uint8_t* Kt = &smem[j & 1][0][0];
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
+    if constexpr (F8) {
+#pragma unroll
+      for (int ks = 0; ks < K8S; ++ks) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int r = 32 * rb + lr;
+          const int c0 = (4 * ks + 2 * hh) ^ GK::swz_k(r), c1 = (4 * ks + 2 * hh + 1) ^ GK::swz_k(r);
+          const u32x4 k0 = *reinterpret_cast<const u32x4*>(Kt + r * KROWB + 16 * c0);
+          const u32x4 k1 = *reinterpret_cast<const u32x4*>(Kt + r * KROWB + 16 * c1);
+          sacc[rb] = mfma32_fp8(k0, k1, qf8[ks], sacc[rb]);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -472,11 +539,12 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
     row_max(jj, sc, false);
     qk(jj + 1, sn);
     softmax_pv(jj, sc);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 K reads
+    constexpr int kQkMfma = F8 ? 2 * K8S : 2 * KS, kKReads = F8 ? 2 : 1;  // per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKReads, 0);  // K reads ahead
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA of Q K^T
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 K read
+    for (int i = 0; i < kQkMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // 1 MFMA of Q K^T
+      __builtin_amdgcn_sched_group_barrier(0x100, kKReads, 0);  // its K reads
     }
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
@@ -514,7 +582,7 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
   // epilogue: O = O_acc / l ; lse = (m + log2 l) ln 2
   const float l_tot = sum_pair32(lsum);
   if (qi >= a.N) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (F8 ? a.v_scale : 1.f);
   const size_t orow = (((size_t)b * a.H_q + h) * a.N + qi) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)

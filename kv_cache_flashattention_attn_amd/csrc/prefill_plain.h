@@ -26,6 +26,7 @@ struct PrefillArgs {
   int B, H_q, H_kv, N;
   float scale_log2;  // scale * log2(e)
   int out_fp32;
+  float v_scale = 1.f;  // FP8 inputs: V's scale, applied to O in the epilogue
 };
 
 template <typename T, int D, bool CAUSAL>

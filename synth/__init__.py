@@ -361,17 +361,19 @@ def int8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
 def fp8_prefill_inputs(case: PrefillCase) -> Dict[str, np.ndarray]:
     """Q, K, V of ``case``'s shapes as OCP FP8 E4M3 codes (uint8), drawn from
     ``SFC64(case.seed + 9000)`` in the order Q, K, V: a random sign, exponent
-    field in [3, 8] and mantissa each (magnitudes 2^-4 .. 3.75)."""
+    field and mantissa each; the exponent field is in [3, 8] for Q and K
+    (magnitudes 2^-4 .. 3.75) and in [3, 7] for V (2^-4 .. 1.875, about the
+    spread of standard-normal draws)."""
     rng = make_rng(case.seed + 9000)
 
-    def codes(shape):
+    def codes(shape, e_hi):
         sgn = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
-        e = rng.integers(3, 9, size=shape, dtype=np.uint8) << 3
+        e = rng.integers(3, e_hi + 1, size=shape, dtype=np.uint8) << 3
         m = rng.integers(0, 8, size=shape, dtype=np.uint8)
         return sgn | e | m
 
-    return {"q": codes((case.B, case.H_q, case.N, case.d)), "k": codes((case.B, case.H_kv, case.N, case.d)),
-            "v": codes((case.B, case.H_kv, case.N, case.d))}
+    return {"q": codes((case.B, case.H_q, case.N, case.d), 8), "k": codes((case.B, case.H_kv, case.N, case.d), 8),
+            "v": codes((case.B, case.H_kv, case.N, case.d), 7)}
 
 
 def tiny_decode_steps(case: PrefillCase = TINY_PREFILL, steps: int = TINY_DECODE_STEPS):
