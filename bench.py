@@ -14,7 +14,9 @@ One step runs every stage of the path once, each on its own workload:
   * fp8      : kv_append_fp8 + attn_decode_paged_fp8, the paged workload with
                the cache stored as OCP FP8 E4M3 (KV GB/s counts 1-byte values);
   * int8     : kv_append_int8 + attn_decode_paged_int8, the same with an int8
-               cache and per-channel scales.
+               cache and per-channel scales;
+  * fp8 prefill: attn_prefill_fp8 on the causal prefill workload with FP8
+               E4M3 Q, K, V (V widened in the call, Q K^T on FP8 MFMA).
 Inputs are seeded synthetic tensors already resident in HBM.  Each kernel call
 is bracketed by HIP events on the stream it runs on.
 
@@ -39,6 +41,10 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill attn TFLOP/s & decode KV GB/s on 1 MI355X (fraction of peak)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+# FP8 prefill: Q K^T (half the FLOPs) on FP8 MFMA, P V (the other half) on bf16
+# MFMA, so its peak is the rate at which both halves would run at their peaks
+PEAK_FP8_PREFILL_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 
 
 def log(*a):
@@ -189,6 +195,14 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty((pcase.B, pcase.H_q, pcase.N), dtype=torch.float32, device="cuda")
     log(f"prefill inputs ready ({time.perf_counter() - t_gen:.1f} s)")
+    # the same workload with FP8 E4M3 inputs
+    f8 = synth.fp8_prefill_inputs(pcase)
+    q8, k8, v8 = (torch.from_numpy(f8[n]).cuda() for n in ("q", "k", "v"))
+    del f8
+    f8_ws = torch.empty(K.attn_prefill_fp8_workspace_bytes(pcase.B, pcase.H_kv, pcase.N, pcase.d), dtype=torch.uint8,
+                        device="cuda")
+    o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+    lse8 = torch.empty_like(lse)
 
     gcase = synth.DECODE_PAGED
     ginp = synth.decode_inputs(gcase)
@@ -248,7 +262,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     legs = ["prefill", "paged_append", "paged_decode", "contig_append", "contig_decode", "chunk_append",
-            "chunk_prefill", "fp8_append", "fp8_decode", "int8_append", "int8_decode"]
+            "chunk_prefill", "fp8_append", "fp8_decode", "int8_append", "int8_decode", "fp8_prefill"]
 
     def step(ev=None):
         def rec(i):
@@ -282,6 +296,9 @@ def main() -> int:
         K.attn_decode_paged_int8(g["q"], i_kp, i_vp, g_table, g_seq, i_ks, i_vs, scale=fcase.sm_scale,
                                  workspace=g_ws, out=i_out)
         rec(11)
+        K.attn_prefill_fp8(q8, k8, v8, causal=True, scale=pcase.sm_scale, q_scale=0.5, k_scale=0.25, v_scale=1.0,
+                           return_lse=True, workspace=f8_ws, out=o8, lse=lse8)
+        rec(12)
 
     if args.calibrate_copy:
         # torch's elementwise multiply: reads 2^30 bytes, writes 2^30 bytes per launch
@@ -322,6 +339,7 @@ def main() -> int:
     k_tflops = k_flops / (ms["chunk_prefill"] * 1e-3) / 1e12
     f_gbs = f_bytes / (ms["fp8_decode"] * 1e-3) / 1e9
     i_gbs = f_bytes / (ms["int8_decode"] * 1e-3) / 1e9  # same 1-byte cache
+    p8_tflops = pf_flops / (ms["fp8_prefill"] * 1e-3) / 1e12
 
     def roof(bound, achieved, peak, unit, kernel, per_unit):
         return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -381,6 +399,13 @@ def main() -> int:
             "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["int8_decode"], 3),
             "roofline": roof("hbm", i_gbs, PEAK_HBM_GBS, "GB/s",
                              "decode_i8_query+decode_mfma_kernel<BF16,128,paged,int8>+merge", {"bytes": f_bytes}),
+        },
+        "prefill_fp8": {
+            "value": round(p8_tflops, 2), "unit": "TFLOP/s", "workload": pcase.name + " (FP8 E4M3 Q, K, V)",
+            "flops": pf_flops, "ms_mean": round(ms["fp8_prefill"], 4), "ms_median": round(med["fp8_prefill"], 4),
+            "speedup_vs_bf16": round(ms["prefill"] / ms["fp8_prefill"], 3),
+            "roofline": roof("mfma", p8_tflops, round(PEAK_FP8_PREFILL_TFLOPS, 1), "TFLOP/s",
+                             "fp8_widen+prefill_mfma_kernel<BF16,128,causal,fp8>", {"flops": pf_flops}),
         },
         "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
         "device_error_flags": flags,
