@@ -358,6 +358,41 @@ def int8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
     return out
 
 
+def int4_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
+                       base: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
+    """Inputs of one decode step over an int4 paged cache with per-channel scales.
+
+    Lengths, block table, q and the new rows as in ``decode_inputs``; from
+    ``SFC64(case.seed + 8500)``: ``k_scales``, ``v_scales`` [H_kv, d] float32,
+    2^u with u uniform in [-5, -2) and, in every KV head, 4 random key channels
+    8x larger; then the pools' packed bytes [num_blocks, H_kv, 16, d / 2], K's
+    then V's: uniform random bytes where a slot holds a token (two uniform codes
+    in [-8, 7] each; -8 never comes out of quantization but decodes like any
+    code); slots holding none carry 0x00 in K and 0x77 (codes 7, 7) in V.
+    """
+    out = dict(base) if base is not None else decode_inputs(case, lens=lens)
+    lens = out["lens"]
+    table = out["block_table"]
+    nblk, Hk, bs, d = out["k_pool"].shape
+    rng = make_rng(case.seed + 8500)
+    ks = np.exp2(rng.uniform(-5.0, -2.0, size=(Hk, d))).astype(np.float32)
+    for h in range(Hk):
+        ks[h, rng.choice(d, size=4, replace=False)] *= np.float32(8.0)
+    vs = np.exp2(rng.uniform(-5.0, -2.0, size=(Hk, d))).astype(np.float32)
+    held = np.zeros((nblk, bs), dtype=bool)
+    for b in range(case.B):
+        L = int(lens[b])
+        nb = -(-L // BLOCK_SIZE)
+        fill = np.clip(L - BLOCK_SIZE * np.arange(nb), 0, BLOCK_SIZE)
+        held[table[b, :nb]] = np.arange(bs)[None, :] < fill[:, None]
+    mask = held[:, None, :, None]
+    shape = (nblk, Hk, bs, d // 2)
+    kp = np.where(mask, rng.integers(0, 256, size=shape, dtype=np.uint8), np.uint8(0x00))
+    vp = np.where(mask, rng.integers(0, 256, size=shape, dtype=np.uint8), np.uint8(0x77))
+    out.update(k_pool=kp.astype(np.uint8), v_pool=vp.astype(np.uint8), k_scales=ks, v_scales=vs)
+    return out
+
+
 def fp8_prefill_inputs(case: PrefillCase) -> Dict[str, np.ndarray]:
     """Q, K, V of ``case``'s shapes as OCP FP8 E4M3 codes (uint8), drawn from
     ``SFC64(case.seed + 9000)`` in the order Q, K, V: a random sign, exponent

@@ -74,3 +74,44 @@ def test_int8_inputs_recipe():
     assert inp["k_pool"].min() >= -127 and inp["v_pool"].min() >= -127
     outliers = inp["k_scales"] >= 2.0 ** -6
     assert outliers.sum(axis=1).tolist() == [4, 4]
+
+
+def test_int4_packing_by_hand():
+    codes = np.array([[1, -1, 7, -7, 0, -8, 3, 4]], np.int8)
+    packed = oracle.pack_int4(codes)
+    # element 2i in the low nibble, 2i + 1 in the high nibble, 4-bit two's complement
+    assert packed.tolist() == [[0xF1, 0x97, 0x80, 0x43]]
+    assert np.array_equal(oracle.unpack_int4(packed), codes)
+    every = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    assert np.array_equal(oracle.pack_int4(oracle.unpack_int4(every)), every)
+
+
+def test_int4_quantize_clamps_to_seven():
+    x = np.array([6.4, 6.5, 7.5, 100.0, -7.5, -100.0, 2.5, np.nan], np.float32).reshape(1, 1, 8)
+    s = np.ones((1, 8), np.float32)
+    assert oracle.quantize_int4(x, "f32", s).ravel().tolist() == [6, 6, 7, 7, -7, -7, 2, 0]
+
+
+def test_int4_decode_step_is_attention_over_dequantized_values():
+    case = synth.DecodeCase("i4", 3, 8, 2, 16, "bf16", 1, 40, True, seed=35)
+    inp = synth.int4_decode_inputs(case)
+    assert inp["k_pool"].shape[-1] == 8
+    cache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
+    O, L = oracle.decode_step_int4(cache, inp["q"], inp["k_new"], inp["v_new"], inp["lens"], case.sm_scale, "bf16",
+                                   inp["k_scales"], inp["v_scales"])
+    for b in range(case.B):
+        n = int(inp["lens"][b]) + 1
+        Kc, Vc = cache.gather(b, n)
+        # nibbles decoded one by one, apart from unpack_int4
+        def val(byte_arr, scales):
+            out = np.empty(byte_arr.shape[:-1] + (2 * byte_arr.shape[-1],))
+            for idx in np.ndindex(byte_arr.shape):
+                byte = int(byte_arr[idx])
+                lo, hi = byte & 15, byte >> 4
+                out[idx[:-1] + (2 * idx[-1],)] = lo - 16 if lo >= 8 else lo
+                out[idx[:-1] + (2 * idx[-1] + 1,)] = hi - 16 if hi >= 8 else hi
+            return out * scales.astype(np.float64)[:, None, :]
+        K, V = val(Kc, inp["k_scales"]), val(Vc, inp["v_scales"])
+        q = oracle.decode_bits(inp["q"][b], "bf16")[None, :, None, :]
+        Oo, Lo = oracle.one_shot(q, K[None], V[None], case.sm_scale)
+        assert np.max(np.abs(O[b] - Oo[0, :, 0])) <= 1e-12 and np.max(np.abs(L[b] - Lo[0, :, 0])) <= 1e-12
