@@ -191,6 +191,31 @@ int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
                        int dtype, void* stream);
 
 /*
+ * kv_append_int4 / attn_decode_paged_int4 -- the int8 cache's scheme at 4 bits.
+ *
+ * Same per-channel scales and rounding as kv_append_int8 with codes clamped to
+ * [-7, 7] (int4 caches: "KV Cache:推理慢的真正原因", 工程优化手段, the
+ * quantization item), two codes per byte: element 2i in the low nibble,
+ * element 2i + 1 in the high nibble, each 4-bit two's complement.  The pools
+ * are bytes [num_blocks, H_kv, 16, d / 2]; a nibble holding -8 (never written
+ * by kv_append_int4) decodes to -8.  Arguments, errors and workspace as for the
+ * int8 calls; attn_decode_paged_int4 takes f16 / bf16 queries at d = 64 or 128.
+ */
+int kv_append_int4(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                   const int32_t* cache_lens, const int32_t* block_table,
+                   int B, int H_kv, int n_new, int d, int block_size,
+                   int max_blocks_per_seq, int num_blocks, int dtype,
+                   const float* k_scales, const float* v_scales, void* stream);
+
+int attn_decode_paged_int4(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           void* o, float* lse,
+                           int B, int H_q, int H_kv, int d, int block_size,
+                           int max_blocks_per_seq, int num_blocks, float scale,
+                           const float* k_scales, const float* v_scales, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_prefill_fp8 -- attn_prefill over FP8 E4M3 inputs.
  *
  * The FP8 attention of FlashAttention-3 ("KV缓存与Flash注意力", the 版本演进

@@ -25,7 +25,8 @@ import torch
 __all__ = [
     "AttnError", "lib", "lib_path", "attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode",
     "attn_decode_paged", "kv_append_fp8", "attn_decode_paged_fp8", "kv_append_int8", "attn_decode_paged_int8",
-    "kv_copy_blocks", "attn_prefill_fp8", "attn_prefill_fp8_workspace_bytes",
+    "kv_copy_blocks", "attn_prefill_fp8", "attn_prefill_fp8_workspace_bytes", "kv_append_int4",
+    "attn_decode_paged_int4",
     "attn_decode_workspace_bytes", "attn_device_error_flags", "attn_version", "DTYPE_CODES",
     "EXPORTED_SYMBOLS",
 ]
@@ -39,7 +40,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3:
           4: "ATTN_ERR_HIP", 5: "ATTN_ERR_NO_BLOCKS"}
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
                     "kv_append_fp8", "attn_decode_paged_fp8", "kv_append_int8", "attn_decode_paged_int8",
-                    "kv_copy_blocks", "attn_prefill_fp8", "attn_prefill_fp8_workspace_bytes",
+                    "kv_copy_blocks", "attn_prefill_fp8", "attn_prefill_fp8_workspace_bytes", "kv_append_int4",
+                    "attn_decode_paged_int4",
                     "attn_decode_workspace_bytes", "attn_last_error", "attn_version",
                     "attn_device_error_flags",
                     "attn_block_pool_create", "attn_block_pool_destroy", "attn_block_pool_free_blocks",
@@ -89,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.kv_append_int8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     L.attn_decode_paged_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp,
                                          vp, i32, vp, sz, vp]
+    L.kv_append_int4.argtypes = L.kv_append_int8.argtypes
+    L.attn_decode_paged_int4.argtypes = L.attn_decode_paged_int8.argtypes
     L.attn_block_pool_create.argtypes = [i32]
     L.attn_block_pool_create.restype = vp
     L.attn_block_pool_destroy.argtypes = [vp]
@@ -101,7 +105,8 @@ def lib() -> ctypes.CDLL:
     L.attn_block_pool_fork.argtypes = [vp, vp, vp, i32, i32]
     for name in ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
                  "kv_append_fp8", "attn_decode_paged_fp8", "attn_device_error_flags", "kv_copy_blocks",
-                 "kv_append_int8", "attn_decode_paged_int8", "attn_prefill_fp8",
+                 "kv_append_int8", "attn_decode_paged_int8", "attn_prefill_fp8", "kv_append_int4",
+                 "attn_decode_paged_int4",
                  "attn_block_pool_free_blocks", "attn_block_pool_holders", "attn_block_pool_reserve",
                  "attn_block_pool_reserve_batch", "attn_block_pool_release", "attn_block_pool_fork"):
         getattr(L, name).restype = i32
@@ -332,23 +337,66 @@ def kv_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tens
     _check("kv_copy_blocks", rc)
 
 
+def _append_int(fn: str, nib: int, k_pool, v_pool, k_new, v_new, cache_lens, block_table, k_scales, v_scales):
+    B, H_kv, n_new, d = k_new.shape
+    nb, _, bs, _ = k_pool.shape
+    if k_pool.shape[-1] * nib != d or v_pool.shape != k_pool.shape:
+        raise ValueError(f"{fn}: pools must be [num_blocks, H_kv, 16, d{'/2' if nib == 2 else ''}]")
+    if k_scales.shape != (H_kv, d) or v_scales.shape != (H_kv, d):
+        raise ValueError("k_scales and v_scales must be [H_kv, d]")
+    rc = getattr(lib(), fn)(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+                            _dev(v_new, "v_new"), _dev(cache_lens, "cache_lens", torch.int32),
+                            _dev(block_table, "block_table", torch.int32), B, H_kv, n_new, d, bs,
+                            block_table.shape[1], nb, _code(k_new), _dev(k_scales, "k_scales", torch.float32),
+                            _dev(v_scales, "v_scales", torch.float32), _stream())
+    _check(fn, rc)
+
+
 def kv_append_int8(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                    cache_lens: torch.Tensor, block_table: torch.Tensor, k_scales: torch.Tensor,
                    v_scales: torch.Tensor) -> None:
     """Quantize and append k_new, v_new [B, H_kv, n_new, d] into int8 pools
     [num_blocks, H_kv, 16, d] with per-channel scales (device fp32 [H_kv, d])."""
-    B, H_kv, n_new, d = k_new.shape
-    nb, _, bs, _ = k_pool.shape
     if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
         raise ValueError("int8 pools are torch.int8 tensors")
+    _append_int("kv_append_int8", 1, k_pool, v_pool, k_new, v_new, cache_lens, block_table, k_scales, v_scales)
+
+
+def kv_append_int4(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   cache_lens: torch.Tensor, block_table: torch.Tensor, k_scales: torch.Tensor,
+                   v_scales: torch.Tensor) -> None:
+    """Quantize and append into int4 pools (torch.uint8 [num_blocks, H_kv, 16, d / 2],
+    two codes per byte) with per-channel scales (device fp32 [H_kv, d])."""
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise ValueError("int4 pools are torch.uint8 tensors of packed codes")
+    _append_int("kv_append_int4", 2, k_pool, v_pool, k_new, v_new, cache_lens, block_table, k_scales, v_scales)
+
+
+def _decode_int(fn: str, nib: int, q, k_pool, v_pool, block_table, seq_lens, k_scales, v_scales, scale, return_lse,
+                workspace, out, lse):
+    B, H_q, d = q.shape
+    nb, H_kv, bs, _ = k_pool.shape
+    if k_pool.shape[-1] * nib != d or v_pool.shape != k_pool.shape:
+        raise ValueError(f"{fn}: pools must be [num_blocks, H_kv, 16, d{'/2' if nib == 2 else ''}]")
     if k_scales.shape != (H_kv, d) or v_scales.shape != (H_kv, d):
         raise ValueError("k_scales and v_scales must be [H_kv, d]")
-    rc = lib().kv_append_int8(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
-                              _dev(v_new, "v_new"), _dev(cache_lens, "cache_lens", torch.int32),
-                              _dev(block_table, "block_table", torch.int32), B, H_kv, n_new, d, bs,
-                              block_table.shape[1], nb, _code(k_new), _dev(k_scales, "k_scales", torch.float32),
-                              _dev(v_scales, "v_scales", torch.float32), _stream())
-    _check("kv_append_int8", rc)
+    mbps = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = attn_decode_workspace_bytes(B, H_q, mbps * bs, d)
+    workspace = _workspace(workspace, nbytes, q.device)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    rc = getattr(lib(), fn)(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                            _dev(block_table, "block_table", torch.int32),
+                            _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
+                            _dev(lse, "lse", torch.float32) if return_lse else 0,
+                            B, H_q, H_kv, d, bs, mbps, nb, scale,
+                            _dev(k_scales, "k_scales", torch.float32),
+                            _dev(v_scales, "v_scales", torch.float32), _code(q),
+                            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream())
+    _check(fn, rc)
+    return (out, lse) if return_lse else out
 
 
 def attn_decode_paged_int8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
@@ -358,30 +406,23 @@ def attn_decode_paged_int8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
                            lse: Optional[torch.Tensor] = None):
     """attn_decode_paged over int8 pools (torch.int8 [num_blocks, H_kv, 16, d])
     with per-channel scales (device fp32 [H_kv, d])."""
-    B, H_q, d = q.shape
-    nb, H_kv, bs, _ = k_pool.shape
-    mbps = block_table.shape[1]
     if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
         raise ValueError("int8 pools are torch.int8 tensors")
-    if k_scales.shape != (H_kv, d) or v_scales.shape != (H_kv, d):
-        raise ValueError("k_scales and v_scales must be [H_kv, d]")
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    nbytes = attn_decode_workspace_bytes(B, H_q, mbps * bs, d)
-    workspace = _workspace(workspace, nbytes, q.device)
-    out = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
-    rc = lib().attn_decode_paged_int8(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-                                      _dev(block_table, "block_table", torch.int32),
-                                      _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
-                                      _dev(lse, "lse", torch.float32) if return_lse else 0,
-                                      B, H_q, H_kv, d, bs, mbps, nb, scale,
-                                      _dev(k_scales, "k_scales", torch.float32),
-                                      _dev(v_scales, "v_scales", torch.float32), _code(q),
-                                      _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                                      _stream())
-    _check("attn_decode_paged_int8", rc)
-    return (out, lse) if return_lse else out
+    return _decode_int("attn_decode_paged_int8", 1, q, k_pool, v_pool, block_table, seq_lens, k_scales, v_scales,
+                       scale, return_lse, workspace, out, lse)
+
+
+def attn_decode_paged_int4(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+                           seq_lens: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
+                           scale: Optional[float] = None, return_lse: bool = False,
+                           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None):
+    """attn_decode_paged over int4 pools (torch.uint8 [num_blocks, H_kv, 16, d / 2])
+    with per-channel scales (device fp32 [H_kv, d])."""
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise ValueError("int4 pools are torch.uint8 tensors of packed codes")
+    return _decode_int("attn_decode_paged_int4", 2, q, k_pool, v_pool, block_table, seq_lens, k_scales, v_scales,
+                       scale, return_lse, workspace, out, lse)
 
 
 def attn_prefill_fp8_workspace_bytes(B: int, H_kv: int, N: int, d: int) -> int:

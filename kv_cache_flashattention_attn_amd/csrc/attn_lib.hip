@@ -259,7 +259,7 @@ int decode_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, int d
 template <typename T, int KV>
 int decode_q8_typed(attn::DecodeArgs a, void* o, float* lse, int d, const CacheQuant& cq, int32_t* cnt,
                     hipStream_t st) {
-  if (KV == attn::kKVInt8) {
+  if (KV == attn::kKVInt8 || KV == attn::kKVInt4) {
     // fold the key scales into an f16 copy of the query, which the decode reads instead
     const int G = a.H_q / a.H_kv;
     if (d == 64)
@@ -281,8 +281,9 @@ int decode_q8_typed(attn::DecodeArgs a, void* o, float* lse, int d, const CacheQ
 template <typename T>
 int decode_q8_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, const CacheQuant& cq, int32_t* cnt,
                        hipStream_t st) {
-  return cq.kind == attn::kKVFp8 ? decode_q8_typed<T, attn::kKVFp8>(a, o, lse, d, cq, cnt, st)
-                                 : decode_q8_typed<T, attn::kKVInt8>(a, o, lse, d, cq, cnt, st);
+  if (cq.kind == attn::kKVFp8) return decode_q8_typed<T, attn::kKVFp8>(a, o, lse, d, cq, cnt, st);
+  if (cq.kind == attn::kKVInt4) return decode_q8_typed<T, attn::kKVInt4>(a, o, lse, d, cq, cnt, st);
+  return decode_q8_typed<T, attn::kKVInt8>(a, o, lse, d, cq, cnt, st);
 }
 
 int check_decode_common(const char* fn, const void* q, const void* k, const void* v, const int32_t* lens,
@@ -463,7 +464,7 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
     if (!std::isfinite(cq.k_scale) || !std::isfinite(cq.v_scale) || !(cq.k_scale > 0.f) || !(cq.v_scale > 0.f))
       return fail(ATTN_ERR_INVALID_ARG, "%s: k_scale and v_scale must be finite and positive", fn);
   }
-  if (cq.kind == attn::kKVInt8) {
+  if (cq.kind == attn::kKVInt8 || cq.kind == attn::kKVInt4) {
     if (!cq.k_scales || !cq.v_scales) return fail(ATTN_ERR_INVALID_ARG, "%s: null scale array", fn);
     if (!aligned16(cq.k_scales) || !aligned16(cq.v_scales))
       return fail(ATTN_ERR_INVALID_ARG, "%s: scale arrays must be 16-byte aligned", fn);
@@ -569,11 +570,33 @@ int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool
                        workspace_bytes_given, stream, cq);
 }
 
+int attn_decode_paged_int4(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d,
+                           int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                           const float* k_scales, const float* v_scales, int dtype, void* workspace,
+                           size_t workspace_bytes_given, void* stream) {
+  if (!block_table) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_int4: null block table");
+  if (block_size != 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_int4: block_size must be 16 (got %d)", block_size);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_int4: max_blocks_per_seq and num_blocks must be >= 1");
+  if ((long long)max_blocks_per_seq * 16 > 0x7FFFFFFFLL)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_int4: max_blocks_per_seq too large");
+  CacheQuant cq;
+  cq.kind = attn::kKVInt4;
+  cq.k_scales = k_scales;
+  cq.v_scales = v_scales;
+  return decode_common("attn_decode_paged_int4", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q,
+                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
+                       workspace_bytes_given, stream, cq);
+}
+
 }  // extern "C"
 
 namespace {
 
-int append_8bit(const char* fn, bool i8, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+// mode: 0 = FP8 E4M3 (per-tensor scales), 1 = int8, 2 = int4 (per-channel scales)
+int append_8bit(const char* fn, int mode, void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                 const int32_t* cache_lens, const int32_t* block_table, int B, int H_kv, int n_new, int d,
                 int block_size, int max_blocks_per_seq, int num_blocks, int dtype, float k_scale, float v_scale,
                 const float* k_scales, const float* v_scales, void* stream) {
@@ -585,6 +608,7 @@ int append_8bit(const char* fn, bool i8, void* k_pool, void* v_pool, const void*
   if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "%s: block_size must be 16 (got %d)", fn, block_size);
   if (max_blocks_per_seq < 1 || num_blocks < 1)
     return fail(ATTN_ERR_INVALID_ARG, "%s: max_blocks_per_seq and num_blocks must be >= 1", fn);
+  const bool i8 = mode != 0;
   if (i8) {
     if (!k_scales || !v_scales) return fail(ATTN_ERR_INVALID_ARG, "%s: null scale array", fn);
     if (!aligned16(k_scales) || !aligned16(v_scales))
@@ -597,10 +621,16 @@ int append_8bit(const char* fn, bool i8, void* k_pool, void* v_pool, const void*
   attn::Append8Args a{static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_new, v_new, cache_lens,
                       block_table, B, H_kv, n_new, d, max_blocks_per_seq, num_blocks,
                       i8 ? 1.f : 1.0f / k_scale, i8 ? 1.f : 1.0f / v_scale, k_scales, v_scales};
-  const long long threads = (long long)B * H_kv * n_new * (d / 8);
+  const long long threads = (long long)B * H_kv * n_new * (d / (mode == 2 ? 16 : 8));
   const dim3 grid((unsigned)((threads + 255) / 256));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (i8) {
+  if (mode == 2) {
+    switch (dtype) {
+      case ATTN_F32: hipLaunchKernelGGL((attn::kv_append_int4_kernel<attn::F32>), grid, dim3(256), 0, st, a); break;
+      case ATTN_F16: hipLaunchKernelGGL((attn::kv_append_int4_kernel<attn::F16>), grid, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((attn::kv_append_int4_kernel<attn::BF16>), grid, dim3(256), 0, st, a); break;
+    }
+  } else if (i8) {
     switch (dtype) {
       case ATTN_F32: hipLaunchKernelGGL((attn::kv_append_8bit_kernel<attn::F32, true>), grid, dim3(256), 0, st, a); break;
       case ATTN_F16: hipLaunchKernelGGL((attn::kv_append_8bit_kernel<attn::F16, true>), grid, dim3(256), 0, st, a); break;
@@ -623,7 +653,7 @@ extern "C" {
 int kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* cache_lens,
                   const int32_t* block_table, int B, int H_kv, int n_new, int d, int block_size,
                   int max_blocks_per_seq, int num_blocks, int dtype, float k_scale, float v_scale, void* stream) {
-  return append_8bit("kv_append_fp8", false, k_pool, v_pool, k_new, v_new, cache_lens, block_table, B, H_kv, n_new,
+  return append_8bit("kv_append_fp8", 0, k_pool, v_pool, k_new, v_new, cache_lens, block_table, B, H_kv, n_new,
                      d, block_size, max_blocks_per_seq, num_blocks, dtype, k_scale, v_scale, nullptr, nullptr,
                      stream);
 }
@@ -632,7 +662,15 @@ int kv_append_int8(void* k_pool, void* v_pool, const void* k_new, const void* v_
                    const int32_t* block_table, int B, int H_kv, int n_new, int d, int block_size,
                    int max_blocks_per_seq, int num_blocks, int dtype, const float* k_scales,
                    const float* v_scales, void* stream) {
-  return append_8bit("kv_append_int8", true, k_pool, v_pool, k_new, v_new, cache_lens, block_table, B, H_kv, n_new,
+  return append_8bit("kv_append_int8", 1, k_pool, v_pool, k_new, v_new, cache_lens, block_table, B, H_kv, n_new,
+                     d, block_size, max_blocks_per_seq, num_blocks, dtype, 1.f, 1.f, k_scales, v_scales, stream);
+}
+
+int kv_append_int4(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* cache_lens,
+                   const int32_t* block_table, int B, int H_kv, int n_new, int d, int block_size,
+                   int max_blocks_per_seq, int num_blocks, int dtype, const float* k_scales,
+                   const float* v_scales, void* stream) {
+  return append_8bit("kv_append_int4", 2, k_pool, v_pool, k_new, v_new, cache_lens, block_table, B, H_kv, n_new,
                      d, block_size, max_blocks_per_seq, num_blocks, dtype, 1.f, 1.f, k_scales, v_scales, stream);
 }
 

@@ -95,7 +95,7 @@ struct DecodeStreamArgs {
 };
 
 // Cache element formats of the decode kernel.
-enum DecKV { kKV16 = 0, kKVFp8 = 1, kKVInt8 = 2 };
+enum DecKV { kKV16 = 0, kKVFp8 = 1, kKVInt8 = 2, kKVInt4 = 3 };
 
 // Sum over the wave (uniform result).
 __device__ __forceinline__ int wave_sum(int x) {
@@ -149,6 +149,26 @@ __device__ __forceinline__ uint32_t i8x2_to_f16(uint32_t xb) {
   const h2 r = __builtin_bit_cast(h2, w) - h2{(_Float16)1152.f, (_Float16)1152.f};
   return __builtin_bit_cast(uint32_t, r);
 }
+// 8 int4 codes (one word: byte b holds elements 2b (low nibble) and 2b + 1)
+// -> 8 f16 values in element order.  With u = code + 8 (one XOR per word), the
+// f16 with bits 0x6400 | u is 1024 + u and the one with 0x6400 | (u << 4) is
+// 1024 + 16 u; one packed f16 FMA, (x * {1, 1/16}) + {-1032, -72}, leaves both
+// codes of a byte exactly.
+__device__ __forceinline__ u32x4 i4x8_to_f16(uint32_t w) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t xb = w ^ 0x88888888u;
+  u32x4 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t bk = (xb >> (8 * k)) & 0xFFu;
+    const uint32_t y = ((bk | (bk << 16)) & 0x00F0000Fu) | 0x64006400u;
+    const h2 r = __builtin_bit_cast(h2, y) * h2{(_Float16)1.f, (_Float16)0.0625f} +
+                 h2{(_Float16)-1032.f, (_Float16)-72.f};
+    out[k] = __builtin_bit_cast(uint32_t, r);
+  }
+  return out;
+}
+
 // 16 int8 codes (words w[0..3]) -> 16 f16 values in two 16-byte vectors
 __device__ __forceinline__ void i8x16_to_f16(const u32x4 w, u32x4& lo, u32x4& hi) {
   const u32x4 b = w ^ 0x80808080u;
@@ -200,16 +220,17 @@ template <typename T, int D, bool PAGED, int KV>
 __global__ void __launch_bounds__(64 * kDecWaves)
 decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const int32_t* __restrict__ table) {
   using Gm = DecGeom<D>;
-  constexpr bool FP8 = KV == kKVFp8, I8 = KV == kKVInt8, Q8 = KV != kKV16;
-  // MFMA operand type: the query's type, except over an int8 cache, where the
+  constexpr bool FP8 = KV == kKVFp8, I8 = KV == kKVInt8, I4 = KV == kKVInt4, Q8 = KV != kKV16;
+  constexpr bool QS = I8 || I4;  // integer codes: key scales folded into an f16 query
+  // MFMA operand type: the query's type, except over an integer cache, where the
   // codes, the scaled query and P are f16 (codes exact, 11-bit products)
-  using TC = typename std::conditional<I8, F16, T>::type;
+  using TC = typename std::conditional<QS, F16, T>::type;
   constexpr int KS = D / 32;   // 32-deep k-steps of Q K^T
   constexpr int DB = D / 16;   // 16-wide blocks of d
   constexpr int ROWB = Gm::ROWB, VCH = Gm::VCH;
   // bytes per cache row, and 16-byte pieces of K and of V a lane loads per stage
-  constexpr int RB = Q8 ? D : ROWB;
-  constexpr int NKL = Q8 ? D / 64 : KS, NVL = Q8 ? D / 64 : VCH;
+  constexpr int RB = I4 ? D / 2 : (Q8 ? D : ROWB);
+  constexpr int NKL = I4 ? 1 : (Q8 ? D / 64 : KS), NVL = I4 ? 1 : (Q8 ? D / 64 : VCH);
 
   __shared__ __attribute__((aligned(1024))) uint8_t vtile[kDecWaves * Gm::SLOT];
 
@@ -335,7 +356,20 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     // contiguous: rows past the capacity (last stage only) read the last row instead
     const int kr = PAGED ? col : min(col, a.capacity - 1 - c.st * kDecStage);
     const int vr = PAGED ? (l >> 2) : min(l >> 2, a.capacity - 1 - c.st * kDecStage);
-    if (Q8) {
+    if constexpr (I4) {
+      // 4-bit rows: the 8-bit assignment at half the bytes (D / 8 bytes of K and
+      // of V per lane: one 16-byte load at d = 128, 8 bytes at d = 64)
+      const uint8_t* ks_src = kp + (row0 + kr) * RB + 4 * KS * grp;
+      const uint8_t* vs_src = vp + (row0 + vr) * RB + (RB / 4) * (l & 3);
+      if constexpr (D == 128) {
+        S.k[0] = *reinterpret_cast<const u32x4*>(ks_src);
+        S.v[0] = *reinterpret_cast<const u32x4*>(vs_src);
+      } else {
+        const u32x2 k2 = *reinterpret_cast<const u32x2*>(ks_src), v2 = *reinterpret_cast<const u32x2*>(vs_src);
+        S.k[0] = u32x4{k2[0], k2[1], 0u, 0u};
+        S.v[0] = u32x4{v2[0], v2[1], 0u, 0u};
+      }
+    } else if (Q8) {
       // 8-bit rows: lane (col, grp) takes the d-chunks KS grp .. KS grp + KS - 1 of
       // its key row (8 KS contiguous bytes); the query fragments use the same
       // assignment of d to k-steps, so the dot products are unchanged.  V: the
@@ -358,17 +392,17 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     if (S.qnew) {
       // query heads g*G + 16 hg + col (columns past the group repeat head g*G)
       const int gi = 16 * hg + col;
-      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (I8 ? 2 * D : D) +
+      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (QS ? 2 * D : D) +
                             (Q8 ? 8 * KS : 8) * grp;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + (Q8 ? 8 : 32) * ks);
-      if constexpr (I8) S.qfac = sa.q_fac[(size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)];
+      if constexpr (QS) S.qfac = sa.q_fac[(size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)];
     }
   };
 
   // per-segment state
   u32x4 qf[KS];
-  u32x4 qlo[I8 ? KS : 1];  // int8: the low f16 parts of the scaled query
+  u32x4 qlo[QS ? KS : 1];  // integer caches: the low f16 parts of the scaled query
   f32x4 oacc[DB];
   float m = kNegInf, lsum = 0.f, lexact = 0.f;
   int piece = 0;
@@ -390,7 +424,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 o = oacc[db] * (FP8 ? inv * sa.v_scale : inv);
-        if constexpr (I8) o *= *reinterpret_cast<const f32x4*>(sa.v_scales + (size_t)g * D + 16 * db + 4 * grp);
+        if constexpr (QS) o *= *reinterpret_cast<const f32x4*>(sa.v_scales + (size_t)g * D + 16 * db + 4 * grp);
         *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = o;
       }
       if (grp == 0) a.part_lse[pidx] = e_tot > 0.f ? (m + __log2f(e_tot)) * kLn2 : kNegInf;
@@ -404,7 +438,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       // that sees a finite score rescales it by exp2(-inf) = 0.
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = S.q[ks];
-      if constexpr (I8) {
+      if constexpr (QS) {
         cl = c_log2 * S.qfac;
         // the low parts, loaded here (segment starts are rare): the wait also
         // covers the next stage's loads, which were issued before this stage's compute
@@ -433,7 +467,16 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     };
     const int t0 = c.st * kDecStage;
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (Q8) {
+    if constexpr (I4) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) put_v(i, i4x8_to_f16(S.v[0][i]));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kw = i4x8_to_f16(S.k[0][ks]);
+        sacc = mfma16k32<TC>(kw, qf[ks], sacc);
+        sacc = mfma16k32<TC>(kw, qlo[ks], sacc);
+      }
+    } else if constexpr (Q8) {
       auto widen = [&](const u32x4 w, u32x4& lo, u32x4& hi) {
         if constexpr (I8) i8x16_to_f16(w, lo, hi);
         else fp8x16_to<T>(w, lo, hi);

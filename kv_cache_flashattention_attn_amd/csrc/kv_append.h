@@ -119,9 +119,9 @@ __device__ __forceinline__ float in_to_f32<F16>(const void* p, int64_t i) {
 // 真正原因", 工程优化手段, the quantization item).  code = rint(x / s[h][c]) in
 // fp32 (the quotient correctly rounded, rint ties to even), clamped to
 // [-127, 127]; NaN -> 0.
-__device__ __forceinline__ uint32_t f32_to_i8(float x, float s) {
+__device__ __forceinline__ uint32_t f32_to_i8(float x, float s, float lim = 127.f) {
   float r = __builtin_rintf(x / s);
-  r = r != r ? 0.f : fminf(fmaxf(r, -127.f), 127.f);
+  r = r != r ? 0.f : fminf(fmaxf(r, -lim), lim);
   return (uint32_t)(int32_t)r & 0xFFu;
 }
 
@@ -185,6 +185,51 @@ __global__ void __launch_bounds__(256) kv_append_8bit_kernel(Append8Args a) {
       kw[e >> 2] |= f32_to_e4m3(in_to_f32<TIN>(a.k_new, src + e) * a.k_inv) << (8 * (e & 3));
       vw[e >> 2] |= f32_to_e4m3(in_to_f32<TIN>(a.v_new, src + e) * a.v_inv) << (8 * (e & 3));
     }
+  }
+  *reinterpret_cast<uint2*>(a.k_pool + dst) = make_uint2(kw[0], kw[1]);
+  *reinterpret_cast<uint2*>(a.v_pool + dst) = make_uint2(vw[0], vw[1]);
+}
+
+// int4 cache: the int8 rule with codes clamped to [-7, 7], two per byte
+// (element 2i in the low nibble, 2i + 1 in the high one, 4-bit two's
+// complement).  One thread quantizes 16 consecutive elements of a K row and of
+// the V row into 8 bytes each.
+template <typename TIN>
+__global__ void __launch_bounds__(256) kv_append_int4_kernel(Append8Args a) {
+  const int per_row = a.d / 16;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.H_kv * a.n_new * per_row;
+  if (idx >= total) return;
+  const int c = (int)(idx % per_row);
+  const int64_t row = idx / per_row;  // ((b*H_kv)+h)*n_new+t
+  const int t = (int)(row % a.n_new);
+  const int h = (int)((row / a.n_new) % a.H_kv);
+  const int b = (int)(row / ((int64_t)a.n_new * a.H_kv));
+  const int start = a.cache_lens[b];
+  if (start < 0) {
+    if (c == 0) raise_device_error(4);
+    return;
+  }
+  const int64_t p = (int64_t)start + t;
+  const int64_t lb = p >> 4;
+  if (lb >= a.max_blocks_per_seq) {
+    if (c == 0) raise_device_error(1);
+    return;
+  }
+  const int blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + lb];
+  if (blk < 0 || blk >= a.num_blocks) {
+    if (c == 0) raise_device_error(2);
+    return;
+  }
+  const int64_t dst = (((int64_t)blk * a.H_kv + h) * 16 + (p & 15)) * (a.d / 2) + 8 * c;
+  const int64_t src = row * a.d + 16 * c;
+  const float* ksc = a.k_scales + (int64_t)h * a.d + 16 * c;
+  const float* vsc = a.v_scales + (int64_t)h * a.d + 16 * c;
+  uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    kw[e >> 3] |= (f32_to_i8(in_to_f32<TIN>(a.k_new, src + e), ksc[e], 7.f) & 0xFu) << (4 * (e & 7));
+    vw[e >> 3] |= (f32_to_i8(in_to_f32<TIN>(a.v_new, src + e), vsc[e], 7.f) & 0xFu) << (4 * (e & 7));
   }
   *reinterpret_cast<uint2*>(a.k_pool + dst) = make_uint2(kw[0], kw[1]);
   *reinterpret_cast<uint2*>(a.v_pool + dst) = make_uint2(vw[0], vw[1]);

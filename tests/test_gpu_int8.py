@@ -1,5 +1,5 @@
-"""GPU parity of the int8 paged KV cache with per-channel scales: quantizing
-append (bit-exact) and decode."""
+"""GPU parity of the int8 and int4 paged KV caches with per-channel scales:
+quantizing append (bit-exact) and decode."""
 import numpy as np
 import pytest
 
@@ -114,5 +114,97 @@ def test_int8_bad_block_raises_flag(K):
     table = inp["block_table"].copy()
     table[1, 0] = -7
     K.attn_decode_paged_int8(to_dev(inp["q"], "bf16"), i8(inp["k_pool"]), i8(inp["v_pool"]), to_dev_i32(table),
+                             to_dev_i32(inp["lens"] + 1), f32(inp["k_scales"]), f32(inp["v_scales"]))
+    assert K.attn_device_error_flags() & 2
+
+
+# ---------------------------------------------------------------- int4
+SPECIAL4 = np.array([2.5, 3.5, -2.5, -0.5, 0.5, 6.5, 7.5, 30.0, -30.0, 0.0, -0.0, 1e-30, np.inf, -np.inf,
+                     np.nan, 0.3, -0.7, 4.0], dtype=np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("pow2", [True, False])
+def test_int4_append_image_is_bit_exact(K, dtype, pow2):
+    case = synth.DecodeCase("i4", 5, 4, 2, 128, dtype, 0, 60, True, 240 + len(dtype), n_new=19)
+    inp = synth.int4_decode_inputs(case)
+    ks, vs = inp["k_scales"].copy(), inp["v_scales"].copy()
+    if pow2:
+        ks, vs = np.exp2(np.round(np.log2(ks))).astype(np.float32), np.exp2(np.round(np.log2(vs))).astype(np.float32)
+    kn, vn = inp["k_new"].copy(), inp["v_new"].copy()
+    n = len(SPECIAL4)
+    kn[0, 0, 0, :n] = synth.to_storage(SPECIAL4 * ks[0, :n], dtype)
+    vn[0, 0, 1, 3:3 + n] = synth.to_storage(SPECIAL4 * vs[0, 3:3 + n], dtype)  # odd offset: high nibbles too
+    kp, vp = u8(inp["k_pool"]), u8(inp["v_pool"])
+    table = to_dev_i32(inp["block_table"])
+    K.kv_append_int4(kp, vp, to_dev(kn, dtype), to_dev(vn, dtype), to_dev_i32(inp["lens"]), table, f32(ks), f32(vs))
+    torch.cuda.synchronize()
+    assert K.attn_device_error_flags() == 0
+    cache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
+    kq = np.stack([oracle.pack_int4(oracle.quantize_int4(kn[b], dtype, ks)) for b in range(case.B)])
+    vq = np.stack([oracle.pack_int4(oracle.quantize_int4(vn[b], dtype, vs)) for b in range(case.B)])
+    cache.append(kq, vq, inp["lens"])
+    if pow2:
+        assert oracle.quantize_int4(kn[0], dtype, ks)[0, 0, :7].tolist() == [2, 4, -2, 0, 0, 6, 7]
+    assert kp.cpu().numpy().tobytes() == cache.k.tobytes(), "K pool image differs"
+    assert vp.cpu().numpy().tobytes() == cache.v.tobytes(), "V pool image differs"
+
+
+def u8(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).cuda()
+
+
+def run_int4(K, case, lens=None, heads=None):
+    print(f"[int4] {case}", flush=True)
+    inp = synth.int4_decode_inputs(case, lens=lens)
+    dt = case.dtype
+    lens_d = to_dev_i32(inp["lens"])
+    kp, vp = u8(inp["k_pool"]), u8(inp["v_pool"])
+    ks, vs = f32(inp["k_scales"]), f32(inp["v_scales"])
+    table = to_dev_i32(inp["block_table"])
+    q = to_dev(inp["q"], dt)
+    K.kv_append_int4(kp, vp, to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt), lens_d, table, ks, vs)
+    o, lse = K.attn_decode_paged_int4(q, kp, vp, table, to_dev_i32(inp["lens"] + 1), ks, vs, scale=case.sm_scale,
+                                      return_lse=True)
+    torch.cuda.synchronize()
+    assert K.attn_device_error_flags() == 0
+    cache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
+    Oref, Lref = oracle.decode_step_int4(cache, inp["q"], inp["k_new"], inp["v_new"], inp["lens"], case.sm_scale, dt,
+                                         inp["k_scales"], inp["v_scales"], heads=heads)
+    assert kp.cpu().numpy().tobytes() == cache.k.tobytes(), "K pool image differs"
+    got_o, got_l = values_of(o), lse.cpu().numpy().astype(np.float64)
+    if heads is not None:
+        idx = tuple(np.array(heads).T)
+        got_o, Oref, got_l, Lref = got_o[idx], Oref[idx], got_l[idx], Lref[idx]
+    assert_close(got_o, Oref, dt)
+    assert_lse_close(got_l, Lref, dt)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_int4_decode_chunk_boundaries(K, d, dtype):
+    lens = np.array([0, 14, 15, 16, 30, 31, 255, 511, 512, 1023, 1500], dtype=np.int32)
+    run_int4(K, synth.DecodeCase("i4", len(lens), 8, 2, d, dtype, 0, 1600, True, 250 + d), lens=lens)
+
+
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
+def test_int4_decode_gqa_groups(K, G):
+    run_int4(K, synth.DecodeCase("i4", 3, 2 * G, 2, 128, "bf16", 1, 700, True, 260 + G))
+
+
+def test_int4_decode_workload_sampled_heads(K):
+    """The paged decode workload (B=64, H_q=32, H_kv=8, lengths 128 .. 8192) with an int4 cache."""
+    c = synth.DECODE_PAGED
+    r = np.random.Generator(np.random.SFC64(433))
+    heads = sorted({(int(b), int(h)) for b, h in zip(r.integers(0, c.B, 40), r.integers(0, c.H_q, 40))})
+    run_int4(K, c, heads=heads)
+
+
+def test_int4_bad_block_raises_flag(K):
+    case = synth.DecodeCase("i4", 2, 4, 2, 64, "bf16", 20, 40, True, 270)
+    inp = synth.int4_decode_inputs(case)
+    table = inp["block_table"].copy()
+    table[1, 0] = -7
+    K.attn_decode_paged_int4(to_dev(inp["q"], "bf16"), u8(inp["k_pool"]), u8(inp["v_pool"]), to_dev_i32(table),
                              to_dev_i32(inp["lens"] + 1), f32(inp["k_scales"]), f32(inp["v_scales"]))
     assert K.attn_device_error_flags() & 2
