@@ -15,6 +15,8 @@ One step runs every stage of the path once, each on its own workload:
                the cache stored as OCP FP8 E4M3 (KV GB/s counts 1-byte values);
   * int8     : kv_append_int8 + attn_decode_paged_int8, the same with an int8
                cache and per-channel scales;
+  * int4     : kv_append_int4 + attn_decode_paged_int4, the same with an int4
+               cache (half a byte per value);
   * fp8 prefill: attn_prefill_fp8 on the causal prefill workload with FP8
                E4M3 Q, K, V (V widened in the call, Q K^T on FP8 MFMA).
 Inputs are seeded synthetic tensors already resident in HBM.  Each kernel call
@@ -258,11 +260,20 @@ def main() -> int:
     i_vs = torch.from_numpy(iinp["v_scales"]).cuda()
     i_out = torch.empty_like(g["q"])
     del iinp
+    # ... and over an int4 cache (two codes per byte)
+    i4inp = synth.int4_decode_inputs(gcase, base=ginp)
+    i4_kp = torch.from_numpy(i4inp["k_pool"]).cuda()
+    i4_vp = torch.from_numpy(i4inp["v_pool"]).cuda()
+    i4_ks = torch.from_numpy(i4inp["k_scales"]).cuda()
+    i4_vs = torch.from_numpy(i4inp["v_scales"]).cuda()
+    i4_out = torch.empty_like(g["q"])
+    del i4inp
     log(f"fp8 decode inputs ready ({time.perf_counter() - t_gen:.1f} s)")
     torch.cuda.synchronize()
 
     legs = ["prefill", "paged_append", "paged_decode", "contig_append", "contig_decode", "chunk_append",
-            "chunk_prefill", "fp8_append", "fp8_decode", "int8_append", "int8_decode", "fp8_prefill"]
+            "chunk_prefill", "fp8_append", "fp8_decode", "int8_append", "int8_decode", "fp8_prefill",
+            "int4_append", "int4_decode"]
 
     def step(ev=None):
         def rec(i):
@@ -299,6 +310,11 @@ def main() -> int:
         K.attn_prefill_fp8(q8, k8, v8, causal=True, scale=pcase.sm_scale, q_scale=0.5, k_scale=0.25, v_scale=1.0,
                            return_lse=True, workspace=f8_ws, out=o8, lse=lse8)
         rec(12)
+        K.kv_append_int4(i4_kp, i4_vp, g["k_new"], g["v_new"], g_lens, g_table, i4_ks, i4_vs)
+        rec(13)
+        K.attn_decode_paged_int4(g["q"], i4_kp, i4_vp, g_table, g_seq, i4_ks, i4_vs, scale=fcase.sm_scale,
+                                 workspace=g_ws, out=i4_out)
+        rec(14)
 
     if args.calibrate_copy:
         # torch's elementwise multiply: reads 2^30 bytes, writes 2^30 bytes per launch
@@ -340,6 +356,8 @@ def main() -> int:
     f_gbs = f_bytes / (ms["fp8_decode"] * 1e-3) / 1e9
     i_gbs = f_bytes / (ms["int8_decode"] * 1e-3) / 1e9  # same 1-byte cache
     p8_tflops = pf_flops / (ms["fp8_prefill"] * 1e-3) / 1e12
+    i4_bytes = f_bytes // 2  # half a byte per value
+    i4_gbs = i4_bytes / (ms["int4_decode"] * 1e-3) / 1e9
 
     def roof(bound, achieved, peak, unit, kernel, per_unit):
         return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -399,6 +417,14 @@ def main() -> int:
             "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["int8_decode"], 3),
             "roofline": roof("hbm", i_gbs, PEAK_HBM_GBS, "GB/s",
                              "decode_i8_query+decode_mfma_kernel<BF16,128,paged,int8>+merge", {"bytes": f_bytes}),
+        },
+        "decode_paged_int4": {
+            "value": round(i4_gbs, 1), "unit": "GB/s", "workload": fcase.name + " (int4 cache, per-channel scales)",
+            "kv_bytes": i4_bytes, "ms_mean": round(ms["int4_decode"], 4), "ms_median": round(med["int4_decode"], 4),
+            "append_ms": round(ms["int4_append"], 4),
+            "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["int4_decode"], 3),
+            "roofline": roof("hbm", i4_gbs, PEAK_HBM_GBS, "GB/s",
+                             "decode_i8_query+decode_mfma_kernel<BF16,128,paged,int4>+merge", {"bytes": i4_bytes}),
         },
         "prefill_fp8": {
             "value": round(p8_tflops, 2), "unit": "TFLOP/s", "workload": pcase.name + " (FP8 E4M3 Q, K, V)",
