@@ -275,6 +275,14 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
     const int blk = j < kLdsBlocks ? __builtin_amdgcn_readfirstlane(blk_lds[j]) : checked_block(j);
     return min(max(blk, 0), pk.num_blocks - 1);  // already valid; kept inside the pool regardless
   };
+  // paged full tiles: copy i of wave w covers rows w * RPC + i * NW * RPC of the
+  // tile, i.e. block slot pw_slot + i * kSlotStep, rows starting at row
+  // (w * RPC) % 16 of that block (NW * RPC is a multiple of 16)
+  const int pw = w & (NW - 1);
+  const int pw_slot = (pw * Gm::ROWS_PER_COPY) >> 4;
+  constexpr int kSlotStep = NW * Gm::ROWS_PER_COPY / 16;
+  const uint64_t pw_off = ((uint64_t)g * 16 + ((pw * Gm::ROWS_PER_COPY) & 15)) * ROWB;
+  const uint32_t blk_bytes = (uint32_t)a.H_kv * 16 * ROWB;  // one block, all KV heads (< 2^28)
   auto issue_paged = [&](const uint16_t* src, const uint32_t ch, int which, int k0, int buf) {
     const uint32_t dst = smem_base + (2 * buf + which) * TILE + w * 1024;
     const uint8_t* base = reinterpret_cast<const uint8_t*>(src);
@@ -292,10 +300,24 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
 #pragma unroll
       for (int u = 0; u < 4; ++u) ids[u] = (j0 + u) * 16 <= last ? checked_block(j0 + u) : 0;
     }
-    const bool ragged = k0 + BN > Nk;
-    // rows past the last key read the last key instead (ragged last tile only)
-    const int blk_last = ragged ? min(max(block_at(last), 0), pk.num_blocks - 1) : 0;
     const uint32_t lane_off = (l / CH) * ROWB + ch;  // this lane's bytes within the copy's rows
+    if (k0 + BN <= Nk) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ids[u] = min(max(ids[u], 0), pk.num_blocks - 1);  // valid already; kept in the pool
+      // full tile: copy i fills rows of block slot pw_slot + i * kSlotStep, at the
+      // wave's fixed row offset within the block; the scalar base is the block's
+      // offset (one 32 x 32 -> 64-bit product) plus a per-wave constant
+#pragma unroll
+      for (int i = 0; i < Gm::COPIES; ++i) {
+        const int slot = pw_slot + i * kSlotStep;  // 0 .. 3, wave-uniform
+        const int blk = slot == 0 ? ids[0] : slot == 1 ? ids[1] : slot == 2 ? ids[2] : ids[3];
+        const uint8_t* cb = base + pw_off + (uint64_t)(uint32_t)blk * blk_bytes;
+        lds_copy16(cb, lane_off, dst + i * kCopyStride);
+      }
+      return;
+    }
+    // ragged last tile: rows past the last key read the last key instead
+    const int blk_last = min(max(block_at(last), 0), pk.num_blocks - 1);
 #pragma unroll
     for (int i = 0; i < Gm::COPIES; ++i) {
       // the copy's ROWS_PER_COPY rows lie in one 16-row block of the tile
@@ -303,16 +325,10 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
       const int slot = (fr >> 4) - j0;  // 0 .. 3, wave-uniform
       int blk = slot == 0 ? ids[0] : slot == 1 ? ids[1] : slot == 2 ? ids[2] : ids[3];
       blk = min(max(blk, 0), pk.num_blocks - 1);  // valid already; kept inside the pool regardless
-      if (!ragged) {
-        // wave-uniform row base (scalar registers) plus one lane offset
-        const uint8_t* cb = base + (((size_t)blk * a.H_kv + g) * 16 + (fr & 15)) * ROWB;
-        lds_copy16(cb, lane_off, dst + i * kCopyStride);
-      } else {
-        const int r = fr + l / CH;
-        const bool in = r <= last;
-        const size_t row = ((size_t)(in ? blk : blk_last) * a.H_kv + g) * 16 + ((in ? r : last) & 15);
-        lds_copy16(base + row * ROWB + ch, dst + i * kCopyStride);
-      }
+      const int r = fr + l / CH;
+      const bool in = r <= last;
+      const size_t row = ((size_t)(in ? blk : blk_last) * a.H_kv + g) * 16 + ((in ? r : last) & 15);
+      lds_copy16(base + row * ROWB + ch, dst + i * kCopyStride);
     }
   };
   auto issue = [&](const uint16_t* src, const uint32_t off, int which, int k0, int buf) {
