@@ -105,6 +105,28 @@ def test_paged_identity_table_matches_contiguous(K):
     assert torch.equal(op.view(torch.int16), oc.view(torch.int16))
 
 
+def test_decode_repeatable(K):
+    """The same inputs give the same bits on every call (each call on fresh copies of the cache)."""
+    B, H_kv, H_q, d, nb = 2, 2, 8, 128, 6
+    r = np.random.Generator(np.random.SFC64(51))
+    pool_k = synth.to_storage(r.standard_normal((B * nb, H_kv, 16, d), dtype=np.float32), "bf16")
+    pool_v = synth.to_storage(r.standard_normal((B * nb, H_kv, 16, d), dtype=np.float32), "bf16")
+    qn = synth.to_storage(r.standard_normal((B, H_q, d), dtype=np.float32), "bf16")
+    table = np.arange(B * nb, dtype=np.int32).reshape(B, nb)
+    contig_k = np.ascontiguousarray(pool_k.reshape(B, nb, H_kv, 16, d).transpose(0, 2, 1, 3, 4).reshape(B, H_kv, nb * 16, d))
+    contig_v = np.ascontiguousarray(pool_v.reshape(B, nb, H_kv, 16, d).transpose(0, 2, 1, 3, 4).reshape(B, H_kv, nb * 16, d))
+    lens = to_dev_i32(np.array([nb * 16, 37], dtype=np.int32))
+    q = to_dev(qn, "bf16")
+    outs = []
+    for _ in range(8):
+        oc = K.attn_decode(q, to_dev(contig_k, "bf16"), to_dev(contig_v, "bf16"), lens)
+        op = K.attn_decode_paged(q, to_dev(pool_k, "bf16"), to_dev(pool_v, "bf16"), to_dev_i32(table), lens)
+        torch.cuda.synchronize()
+        outs.append((bits_of(oc), bits_of(op)))
+    for oc, op in outs:
+        assert np.array_equal(oc, outs[0][0]) and np.array_equal(op, outs[0][0])
+
+
 def test_decode_zero_length_gives_zero(K):
     lens = np.array([0, 5], dtype=np.int32)
     c = case(False, 2, 4, 2, 128, "bf16", 0, 10, 60)
