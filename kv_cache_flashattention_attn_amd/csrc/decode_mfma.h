@@ -390,13 +390,17 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       // 8-bit rows: lane (col, grp) takes the d-chunks KS grp .. KS grp + KS - 1 of
       // its key row (8 KS contiguous bytes); the query fragments use the same
       // assignment of d to k-steps, so the dot products are unchanged.  V: the
-      // same rows and columns as the 16-bit layout, a quarter row per lane.
+      // stage's rows are contiguous: instruction i of lane l moves their bytes
+      // 16 l + 1024 i (whole cache lines): row l / (RB / 16) + i 1024 / RB.
       const uint8_t* ks_src = kp + (row0 + kr) * RB + 8 * KS * grp;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) S.k[i] = load_stream(ks_src + 16 * i);
-      const uint8_t* vs_src = vp + (row0 + vr) * RB + (RB / 4) * (l & 3);
+      const int lim = PAGED ? kDecStage - 1 : a.capacity - 1 - c.st * kDecStage;
 #pragma unroll
-      for (int i = 0; i < NVL; ++i) S.v[i] = load_stream(vs_src + 16 * i);
+      for (int i = 0; i < NVL; ++i) {
+        const int r = min(l / (RB / 16) + i * (1024 / RB), lim);
+        S.v[i] = load_stream(vp + (row0 + r) * RB + 16 * (l % (RB / 16)));
+      }
     } else {
       // 16-bit rows.  K goes straight into MFMA operand registers (each load
       // instruction covers half of every row's 128-byte lines, the next one
@@ -511,12 +515,15 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
         if constexpr (I8) i8x16_to_f16(w, lo, hi);
         else fp8x16_to<T>(w, lo, hi);
       };
+      // V: 16 values of row r at columns 16 (l % (RB / 16)), i.e. logical
+      // 16-bit chunks 2 (l % (RB / 16)) and the next one
 #pragma unroll
       for (int i = 0; i < NVL; ++i) {
         u32x4 lo, hi;
         widen(S.v[i], lo, hi);
-        put_v(2 * i, lo);
-        put_v(2 * i + 1, hi);
+        const int r = l / (RB / 16) + i * (1024 / RB), ch = 2 * (l % (RB / 16));
+        *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * (ch ^ Gm::swz_v(r))) = lo;
+        *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ((ch + 1) ^ Gm::swz_v(r))) = hi;
       }
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
