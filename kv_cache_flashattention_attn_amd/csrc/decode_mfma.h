@@ -260,6 +260,15 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   const int n_workers = gridDim.x * kDecWaves;
 
   auto clamp = [&](int n) { return n < 0 ? 0 : (n > a.capacity ? a.capacity : n); };
+  // d of the 8 values lane group grp contributes to k-step ks of Q K^T (K and
+  // the query fragments agree on it): 16-bit rows 32 ks + 8 grp; 8-bit rows
+  // 64 (ks / 2) + 16 grp + 8 (ks % 2) (each K load is 64 contiguous bytes of a
+  // row, widened into k-steps 2i and 2i + 1); 4-bit rows 8 KS grp + 8 ks.
+  auto qd = [&](int ks) {
+    if constexpr (I4) return 8 * KS * grp + 8 * ks;
+    else if constexpr (Q8) return 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1);
+    else return 32 * ks + 8 * grp;
+  };
   auto stages_of = [&](int len) { return (len + kDecStage - 1) / kDecStage; };
 
   // total stages (lanes read 64 lengths at a time) and this wave's share
@@ -387,14 +396,15 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
         S.v[0] = u32x4{v2[0], v2[1], 0u, 0u};
       }
     } else if (Q8) {
-      // 8-bit rows: lane (col, grp) takes the d-chunks KS grp .. KS grp + KS - 1 of
-      // its key row (8 KS contiguous bytes); the query fragments use the same
-      // assignment of d to k-steps, so the dot products are unchanged.  V: the
-      // stage's rows are contiguous: instruction i of lane l moves their bytes
+      // 8-bit rows: load i of lane (col, grp) takes bytes 64 i + 16 grp of key
+      // row col, so one instruction covers 64 contiguous bytes of every row (as
+      // the 16-bit K loads do); the query fragments use the same assignment of
+      // d to k-steps (qd), so the dot products are unchanged.  V: the stage's
+      // rows are contiguous: instruction i of lane l moves their bytes
       // 16 l + 1024 i (whole cache lines): row l / (RB / 16) + i 1024 / RB.
-      const uint8_t* ks_src = kp + (row0 + kr) * RB + 8 * KS * grp;
+      const uint8_t* ks_src = kp + (row0 + kr) * RB + 16 * grp;
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) S.k[i] = load_stream(ks_src + 16 * i);
+      for (int i = 0; i < NKL; ++i) S.k[i] = load_stream(ks_src + 64 * i);
       const int lim = PAGED ? kDecStage - 1 : a.capacity - 1 - c.st * kDecStage;
 #pragma unroll
       for (int i = 0; i < NVL; ++i) {
@@ -423,10 +433,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     if (S.qnew) {
       // query heads g*G + 16 hg + col (columns past the group repeat head g*G)
       const int gi = 16 * hg + col;
-      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (QS ? 2 * D : D) +
-                            (Q8 ? 8 * KS : 8) * grp;
+      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (QS ? 2 * D : D);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + (Q8 ? 8 : 32) * ks);
+      for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + qd(ks));
       if constexpr (QS) S.qfac = sa.q_fac[(size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)];
     }
   };
@@ -475,9 +484,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
         // the low parts, loaded here (segment starts are rare): the wait also
         // covers the next stage's loads, which were issued before this stage's compute
         const int g = c.gh / sa.n_hg, gi = 16 * (c.gh % sa.n_hg) + col;
-        const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (2 * D) + D + 8 * KS * grp;
+        const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (2 * D) + D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qlo[ks] = *reinterpret_cast<const u32x4*>(src + 8 * ks);
+        for (int ks = 0; ks < KS; ++ks) qlo[ks] = *reinterpret_cast<const u32x4*>(src + qd(ks));
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       }
       m = kNegInf;
