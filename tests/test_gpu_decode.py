@@ -127,6 +127,32 @@ def test_decode_repeatable(K):
         assert np.array_equal(oc, outs[0][0]) and np.array_equal(op, outs[0][0])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_contiguous_capacity_not_multiple_of_16(K, d):
+    """A contiguous cache of 37 rows: the last 16-token stage reaches past the capacity
+    (those rows are read from the last row and masked)."""
+    B, H_kv, H_q, cap = 3, 2, 8, 37
+    r = np.random.Generator(np.random.SFC64(70 + d))
+    kc = synth.to_storage(r.standard_normal((B, H_kv, cap, d), dtype=np.float32), "bf16")
+    vc = synth.to_storage(r.standard_normal((B, H_kv, cap, d), dtype=np.float32), "bf16")
+    qn = synth.to_storage(r.standard_normal((B, H_q, d), dtype=np.float32), "bf16")
+    lens = np.array([37, 33, 16], dtype=np.int32)
+    print(f"[decode] contiguous capacity {cap}, d={d}, lens={lens.tolist()}", flush=True)
+    o, lse = K.attn_decode(to_dev(qn, "bf16"), to_dev(kc, "bf16"), to_dev(vc, "bf16"), to_dev_i32(lens),
+                           return_lse=True)
+    torch.cuda.synchronize()
+    assert K.attn_device_error_flags() == 0
+    Q, Kk, V = (oracle.decode_bits(x, "bf16") for x in (qn, kc, vc))
+    Oref = np.zeros((B, H_q, d))
+    Lref = np.zeros((B, H_q))
+    for b in range(B):
+        L = int(lens[b])
+        ob, lb = oracle.one_shot(Q[b:b + 1, :, None, :], Kk[b:b + 1, :, :L], V[b:b + 1, :, :L], 1 / np.sqrt(d))
+        Oref[b], Lref[b] = ob[0, :, 0], lb[0, :, 0]
+    assert_close(values_of(o), Oref, "bf16")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), Lref, "bf16")
+
+
 def test_decode_zero_length_gives_zero(K):
     lens = np.array([0, 5], dtype=np.int32)
     c = case(False, 2, 4, 2, 128, "bf16", 0, 10, 60)
