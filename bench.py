@@ -124,6 +124,49 @@ def block_pool_leg() -> dict:
     return out
 
 
+def sample_clock(run, seconds: float, torch):
+    """Run ``run()`` back to back for ``seconds`` while a thread reads the GPU's
+    current graphics clock and socket power (amdsmi GPU metrics, every 10 ms).
+    Returns the medians over the second half of the samples (the clock settles
+    after the first few hundred ms), or None when amdsmi is unavailable."""
+    try:
+        import threading
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        amdsmi.amdsmi_get_gpu_metrics_info(handle)
+    except Exception as e:  # metrics are optional context, never a reason to fail
+        log(f"GPU clock not recorded: {e!r}")
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                clk, pw = m.get("current_gfxclk"), m.get("current_socket_power")
+                if isinstance(clk, (int, float)) and isinstance(pw, (int, float)):
+                    samples.append((clk, pw))
+            except Exception:
+                pass
+            time.sleep(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    tail = samples[len(samples) // 2:]
+    if not tail:
+        return None
+    return {"gfxclk_mhz": float(np.median([c for c, _ in tail])),
+            "socket_power_w": float(np.median([p for _, p in tail])), "samples": len(tail)}
+
+
 def cpu_baseline(seconds: float, prefill_case, prefill_raw, paged_case, paged_inp):
     """The fp64 oracle as it stands, on a bounded sample of the same workloads."""
     import oracle
@@ -173,6 +216,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle time budget (0 = skip)")
+    ap.add_argument("--clock-seconds", type=float, default=1.5,
+                    help="per leg: run prefill, then paged decode, alone this long while sampling the GPU clock (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write kernel (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -437,6 +482,17 @@ def main() -> int:
         "device_error_flags": flags,
         "kernel_source_hash": kernel_source_hash(),
     }
+    # clock and power while one leg runs alone (after the timed steps; context
+    # for the fractions of peak, which assume the 2.4 GHz peak clock)
+    if args.clock_seconds > 0:
+        clk_pf = sample_clock(lambda: K.attn_prefill(q, k, v, causal=True, scale=pcase.sm_scale, return_lse=True,
+                                                     out=o, lse=lse), args.clock_seconds, torch)
+        clk_dec = sample_clock(lambda: K.attn_decode_paged(g["q"], g["k_pool"], g["v_pool"], g_table, g_seq,
+                                                           scale=gcase.sm_scale, workspace=g_ws, out=g_out),
+                               args.clock_seconds, torch)
+        result["clock"] = {"prefill": clk_pf, "decode_paged": clk_dec, "peak_gfxclk_mhz": 2400,
+                           "source": "amdsmi current_gfxclk / current_socket_power, sampled every 10 ms while "
+                                     "the leg runs alone after the timed steps; median of the second half"}
     result["block_pool"] = block_pool_leg()
     if args.cpu_seconds > 0:
         log("timing the CPU oracle on a bounded sample ...")
