@@ -500,9 +500,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       if (piece == 0 && l == 0)
         sa.piece_cnt[(size_t)c.b * a.H_q + c.gh] = (seg0 + c.n - 1) / share - seg0 / share + 1;
     }
-    // V rows into the LDS tile (row l / 4, logical chunks VCH (l % 4) + i), and
-    // S^T = K Q^T: lane holds head col, tokens t0 + 4 grp + i.  An FP8 stage is
-    // first widened to 16-bit values.
+    // V rows into the LDS tile, and S^T = K Q^T: lane holds head col, tokens
+    // t0 + 4 grp + i.  An 8- or 4-bit stage is first widened to 16-bit values.
+    // put_v: the 4-bit layout (lane -> row l / 4, logical chunks VCH (l % 4) + i).
     auto put_v = [&](const int i, const u32x4 x) {
       const int r = l >> 2;
       const int ch = (VCH * (l & 3) + i) ^ Gm::swz_v(r);
