@@ -18,7 +18,9 @@ One step runs every stage of the path once, each on its own workload:
   * int4     : kv_append_int4 + attn_decode_paged_int4, the same with an int4
                cache (half a byte per value);
   * fp8 prefill: attn_prefill_fp8 on the causal prefill workload with FP8
-               E4M3 Q, K, V (V widened in the call, Q K^T on FP8 MFMA).
+               E4M3 Q, K, V (V widened in the call, Q K^T on FP8 MFMA);
+  * f16 prefill: fp16 non-causal attention, B=1, H=8, N=1024, d=64 (a small
+               case: 64 query blocks for 256 CUs).
 Inputs are seeded synthetic tensors already resident in HBM.  Each kernel call
 is bracketed by HIP events on the stream it runs on.
 
@@ -241,6 +243,12 @@ def main() -> int:
     q, k, v = (to_dev(praw[n], pcase.dtype, torch) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty((pcase.B, pcase.H_q, pcase.N), dtype=torch.float32, device="cuda")
+    # the fp16 non-causal prefill 1x8x1024x64 (a small case: 64 query blocks of 128 rows)
+    scase = synth.PREFILL_F16
+    sraw = synth.prefill_inputs(scase)
+    q2, k2, v2 = (to_dev(sraw[n], scase.dtype, torch) for n in ("q", "k", "v"))
+    o2 = torch.empty_like(q2)
+    del sraw
     log(f"prefill inputs ready ({time.perf_counter() - t_gen:.1f} s)")
     # the same workload with FP8 E4M3 inputs
     f8 = synth.fp8_prefill_inputs(pcase)
@@ -318,7 +326,7 @@ def main() -> int:
 
     legs = ["prefill", "paged_append", "paged_decode", "contig_append", "contig_decode", "chunk_append",
             "chunk_prefill", "fp8_append", "fp8_decode", "int8_append", "int8_decode", "fp8_prefill",
-            "int4_append", "int4_decode"]
+            "int4_append", "int4_decode", "f16_prefill"]
 
     def step(ev=None):
         def rec(i):
@@ -360,6 +368,8 @@ def main() -> int:
         K.attn_decode_paged_int4(g["q"], i4_kp, i4_vp, g_table, g_seq, i4_ks, i4_vs, scale=fcase.sm_scale,
                                  workspace=g_ws, out=i4_out)
         rec(14)
+        K.attn_prefill(q2, k2, v2, causal=False, scale=scase.sm_scale, out=o2)
+        rec(15)
 
     if args.calibrate_copy:
         # torch's elementwise multiply: reads 2^30 bytes, writes 2^30 bytes per launch
@@ -403,6 +413,7 @@ def main() -> int:
     p8_tflops = pf_flops / (ms["fp8_prefill"] * 1e-3) / 1e12
     i4_bytes = f_bytes // 2  # half a byte per value
     i4_gbs = i4_bytes / (ms["int4_decode"] * 1e-3) / 1e9
+    s_tflops = scase.flops() / (ms["f16_prefill"] * 1e-3) / 1e12
 
     def roof(bound, achieved, peak, unit, kernel, per_unit):
         return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -477,6 +488,13 @@ def main() -> int:
             "speedup_vs_bf16": round(ms["prefill"] / ms["fp8_prefill"], 3),
             "roofline": roof("mfma", p8_tflops, round(PEAK_FP8_PREFILL_TFLOPS, 1), "TFLOP/s",
                              "fp8_widen+prefill_mfma_kernel<BF16,128,causal,fp8>", {"flops": pf_flops}),
+        },
+        "prefill_f16_small": {
+            "value": round(s_tflops, 2), "unit": "TFLOP/s", "workload": scase.name + " (non-causal, no lse)",
+            "flops": scase.flops(), "ms_mean": round(ms["f16_prefill"], 4), "ms_median": round(med["f16_prefill"], 4),
+            "note": "64 workgroups of 128 query rows for 256 CUs",
+            "roofline": roof("mfma", s_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "prefill_mfma_kernel<F16,64,noncausal>",
+                             {"flops": scase.flops()}),
         },
         "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},
         "device_error_flags": flags,
