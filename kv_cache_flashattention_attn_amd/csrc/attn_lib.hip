@@ -263,10 +263,10 @@ int decode_q8_typed(attn::DecodeArgs a, void* o, float* lse, int d, const CacheQ
     // fold the key scales into an f16 copy of the query, which the decode reads instead
     const int G = a.H_q / a.H_kv;
     if (d == 64)
-      hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 64>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
+      hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 64, KV == attn::kKVInt4>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
                          cq.k_scales, cq.q16, cq.q_fac, a.H_q, G);
     else
-      hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 128>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
+      hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 128, KV == attn::kKVInt4>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
                          cq.k_scales, cq.q16, cq.q_fac, a.H_q, G);
     const int rc = launch_status("attn_decode int8 query");
     if (rc != ATTN_OK) return rc;

@@ -166,23 +166,24 @@ __device__ __forceinline__ uint32_t i8x2_to_f16(uint32_t xb) {
   return __builtin_bit_cast(uint32_t, r);
 }
 // 8 int4 codes (one word: byte b holds elements 2b (low nibble) and 2b + 1)
-// -> 8 f16 values in element order.  With u = code + 8 (one XOR per word), the
-// f16 with bits 0x6400 | u is 1024 + u and the one with 0x6400 | (u << 4) is
-// 1024 + 16 u; one packed f16 FMA, (x * {1, 1/16}) + {-1032, -72}, leaves both
-// codes of a byte exactly.
-__device__ __forceinline__ u32x4 i4x8_to_f16(uint32_t w) {
+// -> 8 f16 values in the order e0, e4, e1, e5, e2, e6, e3, e7 (element e in
+// 16-bit slot kI4Slot(e)).  With u = code + 8 (one XOR per word), each 16-bit
+// half of a word takes one nibble with one and-or: the f16 with bits 0x6400 | u
+// is 1024 + u and the one with 0x6400 | (u << 4) is 1024 + 16 u, exactly; one
+// packed f16 add (- 1032) or FMA (* 1/16 - 72) per pair leaves the codes.  The
+// query fragments and the output rows follow the same slot order.
+__device__ __forceinline__ constexpr int kI4Slot(int e) { return ((e & 3) << 1) | (e >> 2); }
+__device__ __forceinline__ u32x4 i4x8_to_f16_slots(uint32_t w) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const uint32_t xb = w ^ 0x88888888u;
-  u32x4 out;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t bk = (xb >> (8 * k)) & 0xFFu;
-    const uint32_t y = ((bk | (bk << 16)) & 0x00F0000Fu) | 0x64006400u;
-    const h2 r = __builtin_bit_cast(h2, y) * h2{(_Float16)1.f, (_Float16)0.0625f} +
-                 h2{(_Float16)-1032.f, (_Float16)-72.f};
-    out[k] = __builtin_bit_cast(uint32_t, r);
-  }
-  return out;
+  const uint32_t xb = w ^ 0x88888888u, x2 = xb >> 8;
+  const h2 t0 = __builtin_bit_cast(h2, (xb & 0x000F000Fu) | 0x64006400u);  // 1024 + u0, 1024 + u4
+  const h2 t1 = __builtin_bit_cast(h2, (xb & 0x00F000F0u) | 0x64006400u);  // 1024 + 16 u1, 1024 + 16 u5
+  const h2 t2 = __builtin_bit_cast(h2, (x2 & 0x000F000Fu) | 0x64006400u);  // 1024 + u2, 1024 + u6
+  const h2 t3 = __builtin_bit_cast(h2, (x2 & 0x00F000F0u) | 0x64006400u);  // 1024 + 16 u3, 1024 + 16 u7
+  const h2 off = h2{(_Float16)1032.f, (_Float16)1032.f};
+  const h2 sixteenth = h2{(_Float16)0.0625f, (_Float16)0.0625f}, off16 = h2{(_Float16)-72.f, (_Float16)-72.f};
+  return u32x4{__builtin_bit_cast(uint32_t, t0 - off), __builtin_bit_cast(uint32_t, t1 * sixteenth + off16),
+               __builtin_bit_cast(uint32_t, t2 - off), __builtin_bit_cast(uint32_t, t3 * sixteenth + off16)};
 }
 
 // 16 int8 codes (words w[0..3]) -> 16 f16 values in two 16-byte vectors
@@ -199,8 +200,10 @@ __device__ __forceinline__ void i8x16_to_f16(const u32x4 w, u32x4& lo, u32x4& hi
 // f16(q' - hi): hi + lo carries about 22 bits, and each part times an integer
 // code is exact in the MFMA's fp32 products.  q16 holds [B][H_q][2][d] (hi row,
 // then lo row); q_fac = 2^(e - 14) undoes the factor in the logit scale.
+// I4SLOTS (int4 cache): within each aligned group of 8 channels, channel e is
+// stored in slot kI4Slot(e), the order in which i4x8_to_f16_slots widens keys.
 // One wave per (head, sequence).
-template <typename T, int D>
+template <typename T, int D, bool I4SLOTS>
 __global__ void __launch_bounds__(64)
 decode_i8_query_kernel(const void* __restrict__ q, const float* __restrict__ k_scales, uint16_t* __restrict__ q16,
                        float* __restrict__ q_fac, int H_q, int G) {
@@ -226,8 +229,10 @@ decode_i8_query_kernel(const void* __restrict__ q, const float* __restrict__ k_s
   for (int e = 0; e < E; ++e) {
     const float x = v[e] * up;
     const uint16_t hi = f32_to_f16_bits(x);
-    dst[l + 64 * e] = hi;
-    dst[D + l + 64 * e] = f32_to_f16_bits(x - f16_bits_to_f32(hi));
+    const int c = l + 64 * e;
+    const int at = I4SLOTS ? ((c & ~7) | kI4Slot(c & 7)) : c;
+    dst[at] = hi;
+    dst[D + at] = f32_to_f16_bits(x - f16_bits_to_f32(hi));
   }
   if (l == 0) q_fac[(size_t)b * H_q + h] = __uint_as_float((uint32_t)(127 - 14 + ex) << 23);
 }
@@ -464,8 +469,18 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 o = oacc[db] * (FP8 ? inv * sa.v_scale : inv);
-        if constexpr (QS) o *= *reinterpret_cast<const f32x4*>(sa.v_scales + (size_t)g * D + 16 * db + 4 * grp);
-        *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = o;
+        if constexpr (I4) {
+          // rows 16 db + 4 grp + i hold slots (4 grp + i) % 8 of their group of 8,
+          // i.e. channels c0 + {0, 4, 1, 5} with c0 = 16 db + 8 (grp / 2) + 2 (grp % 2)
+          const int c0 = 16 * db + 8 * (grp >> 1) + 2 * (grp & 1);
+          const float2 s01 = *reinterpret_cast<const float2*>(sa.v_scales + (size_t)g * D + c0);
+          const float2 s45 = *reinterpret_cast<const float2*>(sa.v_scales + (size_t)g * D + c0 + 4);
+          *reinterpret_cast<float2*>(a.part_o + pidx * D + c0) = float2{o[0] * s01.x, o[2] * s01.y};
+          *reinterpret_cast<float2*>(a.part_o + pidx * D + c0 + 4) = float2{o[1] * s45.x, o[3] * s45.y};
+        } else {
+          if constexpr (QS) o *= *reinterpret_cast<const f32x4*>(sa.v_scales + (size_t)g * D + 16 * db + 4 * grp);
+          *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = o;
+        }
       }
       if (grp == 0) a.part_lse[pidx] = e_tot > 0.f ? (m + __log2f(e_tot)) * kLn2 : kNegInf;
     }
@@ -512,10 +527,10 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (I4) {
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) put_v(i, i4x8_to_f16(S.v[0][i]));
+      for (int i = 0; i < D / 32; ++i) put_v(i, i4x8_to_f16_slots(S.v[0][i]));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kw = i4x8_to_f16(S.k[0][ks]);
+        const u32x4 kw = i4x8_to_f16_slots(S.k[0][ks]);
         sacc = mfma16k32<TC>(kw, qf[ks], sacc);
         sacc = mfma16k32<TC>(kw, qlo[ks], sacc);
       }
