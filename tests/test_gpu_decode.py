@@ -82,6 +82,13 @@ def test_decode_plain_path(K, paged, dtype, d):
 
 
 @pytest.mark.parametrize("paged", [False, True])
+def test_one_long_sequence_many_pieces(K, paged):
+    """One sequence of 40,000 tokens and one KV head: the whole grid shares one
+    segment, cut into ~157 pieces, so the merge combines more than 64 partials."""
+    run_step(K, case(paged, 1, 8, 1, 128, "bf16", 39999, 39999, 90))
+
+
+@pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("n_new", [3, 17])
 def test_multi_token_append(K, paged, n_new):
     run_step(K, case(paged, 4, 8, 4, 128, "bf16", 0, 90, 40 + n_new, n_new=n_new))
