@@ -219,7 +219,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="oracle time budget (0 = skip)")
     ap.add_argument("--clock-seconds", type=float, default=1.5,
-                    help="per leg: run prefill, then paged decode, alone this long while sampling the GPU clock (0 = skip)")
+                    help="per leg: run prefill, then paged decode, alone this long while sampling "
+                         "the GPU clock (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write kernel (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -399,6 +400,11 @@ def main() -> int:
             per[name].append(ev[i].elapsed_time(ev[i + 1]))
     ms = {name: float(np.mean(x)) for name, x in per.items()}
     med = {name: float(np.median(x)) for name, x in per.items()}
+    p10 = {name: float(np.percentile(x, 10)) for name, x in per.items()}
+    p90 = {name: float(np.percentile(x, 90)) for name, x in per.items()}
+
+    def spread(name):
+        return {"ms_p10": round(p10[name], 4), "ms_p90": round(p90[name], 4)}
     flags = K.attn_device_error_flags()
     if flags:
         log(f"WARNING: device error flags {flags}")
@@ -436,10 +442,12 @@ def main() -> int:
         "config": {"workload": pcase.name, "B": pcase.B, "H_q": pcase.H_q, "H_kv": pcase.H_kv, "N": pcase.N,
                    "d": pcase.d, "causal": True, "lse": True, "parallelism": "none (1 GPU)"},
         "roofline": roof("mfma", pf_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "prefill_mfma_kernel<BF16,128,causal>",
-                         {"flops": pf_flops, "ms_mean": round(ms["prefill"], 4), "ms_median": round(med["prefill"], 4)}),
+                         {"flops": pf_flops, "ms_mean": round(ms["prefill"], 4), "ms_median": round(med["prefill"], 4),
+                          **spread("prefill")}),
         "decode_paged": {
             "value": round(g_gbs, 1), "unit": "GB/s", "workload": gcase.name,
             "kv_bytes": g_bytes, "ms_mean": round(ms["paged_decode"], 4), "ms_median": round(med["paged_decode"], 4),
+            **spread("paged_decode"),
             "append_ms": round(ms["paged_append"], 4),
             "roofline": roof("hbm", g_gbs, PEAK_HBM_GBS, "GB/s", "decode_mfma_kernel<BF16,128,paged>+merge",
                              {"bytes": g_bytes}),
@@ -447,6 +455,7 @@ def main() -> int:
         "decode_contig": {
             "value": round(c_gbs, 1), "unit": "GB/s", "workload": ccase.name,
             "kv_bytes": c_bytes, "ms_mean": round(ms["contig_decode"], 4), "ms_median": round(med["contig_decode"], 4),
+            **spread("contig_decode"),
             "append_ms": round(ms["contig_append"], 4),
             "roofline": roof("hbm", c_gbs, PEAK_HBM_GBS, "GB/s", "decode_mfma_kernel<BF16,128,contig>+merge",
                              {"bytes": c_bytes}),
@@ -454,6 +463,7 @@ def main() -> int:
         "chunk_prefill_paged": {
             "value": round(k_tflops, 2), "unit": "TFLOP/s", "workload": kcase.name,
             "flops": k_flops, "ms_mean": round(ms["chunk_prefill"], 4), "ms_median": round(med["chunk_prefill"], 4),
+            **spread("chunk_prefill"),
             "append_ms": round(ms["chunk_append"], 4),
             "roofline": roof("mfma", k_tflops, PEAK_BF16_TFLOPS, "TFLOP/s",
                              "prefill_mfma_kernel<BF16,128,causal,paged>", {"flops": k_flops}),
@@ -461,6 +471,7 @@ def main() -> int:
         "decode_paged_fp8": {
             "value": round(f_gbs, 1), "unit": "GB/s", "workload": fcase.name + " (E4M3 cache)",
             "kv_bytes": f_bytes, "ms_mean": round(ms["fp8_decode"], 4), "ms_median": round(med["fp8_decode"], 4),
+            **spread("fp8_decode"),
             "append_ms": round(ms["fp8_append"], 4),
             "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["fp8_decode"], 3),
             "roofline": roof("hbm", f_gbs, PEAK_HBM_GBS, "GB/s", "decode_mfma_kernel<BF16,128,paged,fp8>+merge",
@@ -469,6 +480,7 @@ def main() -> int:
         "decode_paged_int8": {
             "value": round(i_gbs, 1), "unit": "GB/s", "workload": fcase.name + " (int8 cache, per-channel scales)",
             "kv_bytes": f_bytes, "ms_mean": round(ms["int8_decode"], 4), "ms_median": round(med["int8_decode"], 4),
+            **spread("int8_decode"),
             "append_ms": round(ms["int8_append"], 4),
             "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["int8_decode"], 3),
             "roofline": roof("hbm", i_gbs, PEAK_HBM_GBS, "GB/s",
@@ -477,6 +489,7 @@ def main() -> int:
         "decode_paged_int4": {
             "value": round(i4_gbs, 1), "unit": "GB/s", "workload": fcase.name + " (int4 cache, per-channel scales)",
             "kv_bytes": i4_bytes, "ms_mean": round(ms["int4_decode"], 4), "ms_median": round(med["int4_decode"], 4),
+            **spread("int4_decode"),
             "append_ms": round(ms["int4_append"], 4),
             "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["int4_decode"], 3),
             "roofline": roof("hbm", i4_gbs, PEAK_HBM_GBS, "GB/s",
@@ -485,6 +498,7 @@ def main() -> int:
         "prefill_fp8": {
             "value": round(p8_tflops, 2), "unit": "TFLOP/s", "workload": pcase.name + " (FP8 E4M3 Q, K, V)",
             "flops": pf_flops, "ms_mean": round(ms["fp8_prefill"], 4), "ms_median": round(med["fp8_prefill"], 4),
+            **spread("fp8_prefill"),
             "speedup_vs_bf16": round(ms["prefill"] / ms["fp8_prefill"], 3),
             "roofline": roof("mfma", p8_tflops, round(PEAK_FP8_PREFILL_TFLOPS, 1), "TFLOP/s",
                              "fp8_widen+prefill_mfma_kernel<BF16,128,causal,fp8>", {"flops": pf_flops}),
@@ -492,6 +506,7 @@ def main() -> int:
         "prefill_f16_small": {
             "value": round(s_tflops, 2), "unit": "TFLOP/s", "workload": scase.name + " (non-causal, no lse)",
             "flops": scase.flops(), "ms_mean": round(ms["f16_prefill"], 4), "ms_median": round(med["f16_prefill"], 4),
+            **spread("f16_prefill"),
             "note": "64 workgroups of 128 query rows for 256 CUs",
             "roofline": roof("mfma", s_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "prefill_mfma_kernel<F16,64,noncausal>",
                              {"flops": scase.flops()}),
