@@ -20,7 +20,8 @@ One step runs every stage of the path once, each on its own workload:
   * fp8 prefill: attn_prefill_fp8 on the causal prefill workload with FP8
                E4M3 Q, K, V (V widened in the call, Q K^T on FP8 MFMA);
   * f16 prefill: fp16 non-causal attention, B=1, H=8, N=1024, d=64 (a small
-               case: 64 query blocks for 256 CUs).
+               case: fewer query blocks of 128 rows than CUs, so the key tiles
+               of each 32-row block are split over the waves of a workgroup).
 Inputs are seeded synthetic tensors already resident in HBM.  Each kernel call
 is bracketed by HIP events on the stream it runs on.
 
@@ -507,8 +508,8 @@ def main() -> int:
             "value": round(s_tflops, 2), "unit": "TFLOP/s", "workload": scase.name + " (non-causal, no lse)",
             "flops": scase.flops(), "ms_mean": round(ms["f16_prefill"], 4), "ms_median": round(med["f16_prefill"], 4),
             **spread("f16_prefill"),
-            "note": "64 workgroups of 128 query rows for 256 CUs",
-            "roofline": roof("mfma", s_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "prefill_mfma_kernel<F16,64,noncausal>",
+            "note": "256 workgroups of 32 query rows, each splitting the key tiles over its 4 waves",
+            "roofline": roof("mfma", s_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "prefill_small_kernel<F16,64,noncausal>",
                              {"flops": scase.flops()}),
         },
         "device": {"name": dev_props.name, "cus": dev_props.multi_processor_count},

@@ -20,6 +20,7 @@
 #include "kv_append.h"
 #include "prefill_mfma.h"
 #include "prefill_plain.h"
+#include "prefill_small.h"
 
 namespace {
 
@@ -96,6 +97,28 @@ int resident_grid(const void* kernel, int threads) {
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 
+// Compute units of the current device (0 if the query fails).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
+
+// Small non-causal prefill (d = 64): one workgroup per 32 query rows, key tiles
+// split over its waves (prefill_small.h).
+template <typename T>
+int launch_prefill_small(const attn::PrefillArgs& a, hipStream_t st) {
+  const long long blocks = (long long)((a.N + 31) / 32) * a.B * a.H_q;
+  if (blocks > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: problem too large");
+  const dim3 grid((unsigned)blocks), block(64 * attn::kSmallWaves);
+  if (a.lse != nullptr)
+    hipLaunchKernelGGL((attn::prefill_small_kernel<T, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn::prefill_small_kernel<T, false>), grid, block, 0, st, a);
+  return launch_status("attn_prefill");
+}
+
 // ---------------------------------------------------------------------------
 // prefill dispatch
 // ---------------------------------------------------------------------------
@@ -129,6 +152,12 @@ int launch_prefill_mfma(const attn::PrefillArgs& a, bool causal, hipStream_t st,
   const long long n_qt = (a.N + 32 * NW - 1) / (32 * NW);
   const long long blocks = n_qt * a.B * a.H_q;
   if (blocks > 0x7FFFFFFFLL) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: problem too large");
+  if constexpr (D == 64 && !PAGED && !F8) {
+    // non-causal with fewer query blocks than CUs: split each block's keys over
+    // the waves instead
+    static const int cus = device_cus();  // every device here is an MI355X
+    if (!causal && blocks < cus) return launch_prefill_small<T>(a, st);
+  }
   const dim3 grid((unsigned)blocks), block(64 * NW);
   const bool lse = a.lse != nullptr;
   if (causal && lse)
