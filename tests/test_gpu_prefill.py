@@ -68,6 +68,14 @@ def test_gqa_prefill(K, G, causal):
     run_case(K, 3100 + G, 1, 2 * G, 2, 77, 16, "f32", causal)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gqa_small_noncausal_d64(K, dtype):
+    """Small non-causal d = 64 problems take the key-split kernel: GQA head mapping
+    and ragged tails through it."""
+    run_case(K, 3200, 2, 8, 2, 200, 64, dtype, False)
+    run_case(K, 3201, 1, 4, 1, 1000, 64, dtype, False)
+
+
 def test_fp32_output_mode(K):
     """fp32 output separates arithmetic error from bf16 storage rounding."""
     o = run_case(K, 4000, 1, 4, 4, 513, 128, "bf16", True, out_fp32=True)
