@@ -82,6 +82,15 @@ def test_decode_plain_path(K, paged, dtype, d):
 
 
 @pytest.mark.parametrize("paged", [False, True])
+def test_many_short_sequences(K, paged):
+    """300 sequences of 0 .. 200 cached tokens: most waves cross many segment
+    boundaries (query reload, state reset and a piece write at each)."""
+    o1, _ = run_step(K, case(paged, 300, 32, 8, 128, "bf16", 0, 200, 95))
+    o2, _ = run_step(K, case(paged, 300, 32, 8, 128, "bf16", 0, 200, 95))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("paged", [False, True])
 def test_one_long_sequence_many_pieces(K, paged):
     """One sequence of 40,000 tokens and one KV head: the whole grid shares one
     segment, cut into ~157 pieces, so the merge combines more than 64 partials."""
