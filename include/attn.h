@@ -118,12 +118,16 @@ int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new
 /*
  * attn_decode -- one query per head against a contiguous KV cache.
  *
- *   q, o      : [B, H_q, d]   (the single new query of each head; o same dtype)
+ *   q, o      : [B, H_q, d]   (the single new query of each head; o in dtype,
+ *               or fp32 when out_fp32 != 0: the same result before its rounding
+ *               to dtype, for telling arithmetic error from storage rounding)
  *   k_cache, v_cache : [B, H_kv, max_len, d]
  *   seq_lens  : device int32 [B]; sequence b attends to keys 0 .. seq_lens[b]-1,
  *               i.e. after the append (the decode step concatenates the new
  *               token's K/V before attending, "推理速度慢怎么办？..." section 一).
- *               A length of 0 yields o = 0 and lse = -inf.
+ *               A length of 0 yields o = 0 and lse = -inf.  Slots at or past
+ *               a sequence's length are never weighted and may hold anything,
+ *               NaN and infinities included: they do not reach o or lse.
  *   lse       : [B, H_q] fp32 or NULL.
  *   workspace : device buffer of at least
  *               attn_decode_workspace_bytes(B, H_q, max_len, d) bytes; it holds the
@@ -134,7 +138,7 @@ int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seq_lens, void* o, float* lse,
                 int B, int H_q, int H_kv, int max_len, int d, float scale, int dtype,
-                void* workspace, size_t workspace_bytes, void* stream);
+                int out_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_decode_paged -- attn_decode over a paged KV cache.
@@ -153,7 +157,7 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       void* o, float* lse,
                       int B, int H_q, int H_kv, int d, int block_size,
                       int max_blocks_per_seq, int num_blocks, float scale, int dtype,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      int out_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_prefill_paged -- a chunk of n_new queries per sequence against a paged
@@ -213,7 +217,7 @@ int attn_decode_paged_int4(const void* q, const void* k_pool, const void* v_pool
                            int B, int H_q, int H_kv, int d, int block_size,
                            int max_blocks_per_seq, int num_blocks, float scale,
                            const float* k_scales, const float* v_scales, int dtype,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           int out_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_prefill_fp8 -- attn_prefill over FP8 E4M3 inputs.
@@ -224,7 +228,8 @@ int attn_decode_paged_int4(const void* q, const void* k_pool, const void* v_pool
  * with one fp32 scale per tensor; the result is attention over the
  * dequantized values:
  *   O = softmax(scale * (q_scale Q)(k_scale K)^T) (v_scale V)
- * o [B, H_q, N, d] in out_dtype (F16 or BF16); lse as for attn_prefill.
+ * o [B, H_q, N, d] in out_dtype (F16 or BF16), or fp32 when out_fp32 != 0 (the
+ * same result before its rounding to out_dtype); lse as for attn_prefill.
  * Q K^T runs on the FP8 matrix cores (exact products, fp32 sums).  V's codes
  * are first widened (exactly) into `workspace` as out_dtype values, and P V
  * runs as in the 16-bit kernel, P rounded to out_dtype.
@@ -235,7 +240,7 @@ int attn_decode_paged_int4(const void* q, const void* k_pool, const void* v_pool
 int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H_q, int H_kv, int N, int d, int causal, float scale,
                      float q_scale, float k_scale, float v_scale, int out_dtype,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     int out_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of attn_prefill_fp8: 2 * B * H_kv * N * d (0 on invalid sizes). */
 size_t attn_prefill_fp8_workspace_bytes(int B, int H_kv, int N, int d);
@@ -274,7 +279,7 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
                           int B, int H_q, int H_kv, int d, int block_size,
                           int max_blocks_per_seq, int num_blocks, float scale,
                           float k_scale, float v_scale, int dtype,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          int out_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kv_append_int8 / attn_decode_paged_int8 -- a paged KV cache stored as int8
@@ -317,7 +322,7 @@ int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool
                            int B, int H_q, int H_kv, int d, int block_size,
                            int max_blocks_per_seq, int num_blocks, float scale,
                            const float* k_scales, const float* v_scales, int dtype,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           int out_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kv_copy_blocks -- copy whole physical blocks of the K and V pools.

@@ -74,23 +74,23 @@ def lib() -> ctypes.CDLL:
     L.kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp]
     L.kv_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32,
-                                        f32, i32, vp, sz, vp]
-    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+                                        f32, i32, i32, vp, sz, vp]
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                    vp, sz, vp]
+                                    i32, vp, sz, vp]
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_version.restype = ctypes.c_char_p
     L.attn_device_error_flags.argtypes = [vp]
     L.kv_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
-    L.attn_prefill_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, f32, f32, i32, vp, sz,
-                                   vp]
+    L.attn_prefill_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, f32, f32, i32, i32, vp,
+                                   sz, vp]
     L.attn_prefill_fp8_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.attn_prefill_fp8_workspace_bytes.restype = sz
     L.kv_append_int8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     L.attn_decode_paged_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp,
-                                         vp, i32, vp, sz, vp]
+                                         vp, i32, i32, vp, sz, vp]
     L.kv_append_int4.argtypes = L.kv_append_int8.argtypes
     L.attn_decode_paged_int4.argtypes = L.attn_decode_paged_int8.argtypes
     L.attn_block_pool_create.argtypes = [i32]
@@ -223,24 +223,29 @@ def _workspace(ws: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
     return ws
 
 
+def _out(q: torch.Tensor, shape, out_fp32: bool, dtype=None) -> torch.Tensor:
+    return torch.empty(shape, dtype=torch.float32 if out_fp32 else (dtype or q.dtype), device=q.device)
+
+
 def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
                 scale: Optional[float] = None, return_lse: bool = False,
                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None):
-    """One query per head, q [B, H_q, d], against a contiguous cache [B, H_kv, max_len, d]."""
+                lse: Optional[torch.Tensor] = None, out_fp32: bool = False):
+    """One query per head, q [B, H_q, d], against a contiguous cache [B, H_kv, max_len, d].
+    ``out_fp32``: the output in fp32 (the result before its rounding to q's dtype)."""
     B, H_q, d = q.shape
     _, H_kv, max_len, _ = k_cache.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     nbytes = attn_decode_workspace_bytes(B, H_q, max_len, d)
     workspace = _workspace(workspace, nbytes, q.device)
-    out = torch.empty_like(q) if out is None else out
+    out = _out(q, q.shape, out_fp32) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
     rc = lib().attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
                            _dev(lse, "lse", torch.float32) if return_lse else 0,
-                           B, H_q, H_kv, max_len, d, scale, _code(q), _dev(workspace, "workspace"),
-                           workspace.numel() * workspace.element_size(), _stream())
+                           B, H_q, H_kv, max_len, d, scale, _code(q), int(bool(out_fp32)),
+                           _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream())
     _check("attn_decode", rc)
     return (out, lse) if return_lse else out
 
@@ -248,7 +253,7 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, s
 def attn_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
                       seq_lens: torch.Tensor, scale: Optional[float] = None, return_lse: bool = False,
                       workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                      lse: Optional[torch.Tensor] = None):
+                      lse: Optional[torch.Tensor] = None, out_fp32: bool = False):
     """attn_decode over pools [num_blocks, H_kv, 16, d] and an int32 block table [B, max_blocks]."""
     B, H_q, d = q.shape
     nb, H_kv, bs, _ = k_pool.shape
@@ -256,14 +261,14 @@ def attn_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     nbytes = attn_decode_workspace_bytes(B, H_q, mbps * bs, d)
     workspace = _workspace(workspace, nbytes, q.device)
-    out = torch.empty_like(q) if out is None else out
+    out = _out(q, q.shape, out_fp32) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
     rc = lib().attn_decode_paged(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                                  _dev(block_table, "block_table", torch.int32),
                                  _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
                                  _dev(lse, "lse", torch.float32) if return_lse else 0,
-                                 B, H_q, H_kv, d, bs, mbps, nb, scale, _code(q),
+                                 B, H_q, H_kv, d, bs, mbps, nb, scale, _code(q), int(bool(out_fp32)),
                                  _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                  _stream())
     _check("attn_decode_paged", rc)
@@ -290,7 +295,7 @@ def attn_decode_paged_fp8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
                           seq_lens: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
                           scale: Optional[float] = None, return_lse: bool = False,
                           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                          lse: Optional[torch.Tensor] = None):
+                          lse: Optional[torch.Tensor] = None, out_fp32: bool = False):
     """attn_decode_paged over FP8 E4M3 pools (uint8 [num_blocks, H_kv, 16, d])."""
     B, H_q, d = q.shape
     nb, H_kv, bs, _ = k_pool.shape
@@ -298,7 +303,7 @@ def attn_decode_paged_fp8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     nbytes = attn_decode_workspace_bytes(B, H_q, mbps * bs, d)
     workspace = _workspace(workspace, nbytes, q.device)
-    out = torch.empty_like(q) if out is None else out
+    out = _out(q, q.shape, out_fp32) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
     rc = lib().attn_decode_paged_fp8(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
@@ -306,8 +311,8 @@ def attn_decode_paged_fp8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
                                      _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
                                      _dev(lse, "lse", torch.float32) if return_lse else 0,
                                      B, H_q, H_kv, d, bs, mbps, nb, scale, float(k_scale), float(v_scale), _code(q),
-                                     _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                                     _stream())
+                                     int(bool(out_fp32)), _dev(workspace, "workspace"),
+                                     workspace.numel() * workspace.element_size(), _stream())
     _check("attn_decode_paged_fp8", rc)
     return (out, lse) if return_lse else out
 
@@ -373,7 +378,7 @@ def kv_append_int4(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tens
 
 
 def _decode_int(fn: str, nib: int, q, k_pool, v_pool, block_table, seq_lens, k_scales, v_scales, scale, return_lse,
-                workspace, out, lse):
+                workspace, out, lse, out_fp32=False):
     B, H_q, d = q.shape
     nb, H_kv, bs, _ = k_pool.shape
     if k_pool.shape[-1] * nib != d or v_pool.shape != k_pool.shape:
@@ -384,7 +389,7 @@ def _decode_int(fn: str, nib: int, q, k_pool, v_pool, block_table, seq_lens, k_s
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     nbytes = attn_decode_workspace_bytes(B, H_q, mbps * bs, d)
     workspace = _workspace(workspace, nbytes, q.device)
-    out = torch.empty_like(q) if out is None else out
+    out = _out(q, q.shape, out_fp32) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
     rc = getattr(lib(), fn)(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
@@ -393,7 +398,7 @@ def _decode_int(fn: str, nib: int, q, k_pool, v_pool, block_table, seq_lens, k_s
                             _dev(lse, "lse", torch.float32) if return_lse else 0,
                             B, H_q, H_kv, d, bs, mbps, nb, scale,
                             _dev(k_scales, "k_scales", torch.float32),
-                            _dev(v_scales, "v_scales", torch.float32), _code(q),
+                            _dev(v_scales, "v_scales", torch.float32), _code(q), int(bool(out_fp32)),
                             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream())
     _check(fn, rc)
     return (out, lse) if return_lse else out
@@ -403,26 +408,26 @@ def attn_decode_paged_int8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
                            seq_lens: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
                            scale: Optional[float] = None, return_lse: bool = False,
                            workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                           lse: Optional[torch.Tensor] = None):
+                           lse: Optional[torch.Tensor] = None, out_fp32: bool = False):
     """attn_decode_paged over int8 pools (torch.int8 [num_blocks, H_kv, 16, d])
     with per-channel scales (device fp32 [H_kv, d])."""
     if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
         raise ValueError("int8 pools are torch.int8 tensors")
     return _decode_int("attn_decode_paged_int8", 1, q, k_pool, v_pool, block_table, seq_lens, k_scales, v_scales,
-                       scale, return_lse, workspace, out, lse)
+                       scale, return_lse, workspace, out, lse, out_fp32)
 
 
 def attn_decode_paged_int4(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
                            seq_lens: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
                            scale: Optional[float] = None, return_lse: bool = False,
                            workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                           lse: Optional[torch.Tensor] = None):
+                           lse: Optional[torch.Tensor] = None, out_fp32: bool = False):
     """attn_decode_paged over int4 pools (torch.uint8 [num_blocks, H_kv, 16, d / 2])
     with per-channel scales (device fp32 [H_kv, d])."""
     if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
         raise ValueError("int4 pools are torch.uint8 tensors of packed codes")
     return _decode_int("attn_decode_paged_int4", 2, q, k_pool, v_pool, block_table, seq_lens, k_scales, v_scales,
-                       scale, return_lse, workspace, out, lse)
+                       scale, return_lse, workspace, out, lse, out_fp32)
 
 
 def attn_prefill_fp8_workspace_bytes(B: int, H_kv: int, N: int, d: int) -> int:
@@ -432,9 +437,10 @@ def attn_prefill_fp8_workspace_bytes(B: int, H_kv: int, N: int, d: int) -> int:
 def attn_prefill_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                      scale: Optional[float] = None, q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0,
                      out_dtype=torch.bfloat16, return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
-                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, out_fp32: bool = False):
     """Attention over FP8 E4M3 codes (uint8) q [B, H_q, N, d], k, v [B, H_kv, N, d],
-    each times its scale; the output in out_dtype (torch.bfloat16 or torch.float16)."""
+    each times its scale; the output in out_dtype (torch.bfloat16 or torch.float16),
+    or in fp32 with ``out_fp32`` (the result before its rounding to out_dtype)."""
     B, H_q, N, d = q.shape
     H_kv = k.shape[1]
     if k.shape != (B, H_kv, N, d) or v.shape != k.shape:
@@ -446,13 +452,14 @@ def attn_prefill_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: 
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     nbytes = attn_prefill_fp8_workspace_bytes(B, H_kv, N, d)
     workspace = _workspace(workspace, nbytes, q.device)
-    out = torch.empty((B, H_q, N, d), dtype=out_dtype, device=q.device) if out is None else out
+    out = _out(q, (B, H_q, N, d), out_fp32, out_dtype) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device)
-    rc = lib().attn_prefill_fp8(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out", out_dtype),
+    rc = lib().attn_prefill_fp8(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                _dev(out, "out", torch.float32 if out_fp32 else out_dtype),
                                 _dev(lse, "lse", torch.float32) if return_lse else 0, B, H_q, H_kv, N, d,
                                 int(bool(causal)), scale, float(q_scale), float(k_scale), float(v_scale),
-                                DTYPE_CODES[out_dtype], _dev(workspace, "workspace"),
+                                DTYPE_CODES[out_dtype], int(bool(out_fp32)), _dev(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream())
     _check("attn_prefill_fp8", rc)
     return (out, lse) if return_lse else out

@@ -241,7 +241,7 @@ int launch_merge(const attn::DecodeArgs& a, void* o, float* lse, int chunk, cons
                  hipStream_t st) {
   const int G = a.H_q / a.H_kv;
   attn::MergeArgs m{a.part_o, a.part_lse, a.seq_lens, piece_cnt, o, lse, a.H_q, a.capacity, a.s_max, chunk,
-                    G, (G + 15) / 16};
+                    G, (G + 15) / 16, a.out_fp32};
   hipLaunchKernelGGL((attn::decode_merge_kernel<T, D>), dim3(a.H_q, a.B), dim3(64), 0, st, m);
   return launch_status("attn_decode merge");
 }
@@ -368,7 +368,7 @@ size_t attn_prefill_fp8_workspace_bytes(int B, int H_kv, int N, int d) {
 
 int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H_q, int H_kv, int N,
                      int d, int causal, float scale, float q_scale, float k_scale, float v_scale, int out_dtype,
-                     void* workspace, size_t workspace_bytes_given, void* stream) {
+                     int out_fp32, void* workspace, size_t workspace_bytes_given, void* stream) {
   const char* fn = "attn_prefill_fp8";
   if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
   if (B < 1 || H_q < 1 || H_kv < 1 || N < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: B, H_q, H_kv, N must be >= 1", fn);
@@ -388,7 +388,8 @@ int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, float
   if (!workspace || workspace_bytes_given < need)
     return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes_given);
   if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
-  attn::PrefillArgs a{q, k, v, o, lse, B, H_q, H_kv, N, scale * q_scale * k_scale * attn::kLog2e, 0, v_scale};
+  attn::PrefillArgs a{q, k, v, o, lse, B, H_q, H_kv, N, scale * q_scale * k_scale * attn::kLog2e, out_fp32 != 0,
+                      v_scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
   return out_dtype == ATTN_BF16 ? prefill_fp8_d<attn::BF16>(a, d, causal != 0, workspace, st)
                                 : prefill_fp8_d<attn::F16>(a, d, causal != 0, workspace, st);
@@ -479,7 +480,7 @@ size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d) {
 static int decode_common(const char* fn, bool paged, const void* q, const void* k, const void* v,
                          const int32_t* table, const int32_t* seq_lens, void* o, float* lse, int B, int H_q,
                          int H_kv, int capacity, int mbps, int num_blocks, int d, float scale, int dtype,
-                         void* workspace, size_t workspace_bytes_given, void* stream,
+                         int out_fp32, void* workspace, size_t workspace_bytes_given, void* stream,
                          const CacheQuant& cq = CacheQuant()) {
   int rc = check_decode_common(fn, q, k, v, seq_lens, o, B, H_q, H_kv, d, dtype, scale);
   if (rc != ATTN_OK) return rc;
@@ -522,6 +523,7 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
   a.num_blocks = num_blocks;
   a.s_max = S;
   a.scale_log2 = scale * (cq.kind == attn::kKVFp8 ? cq.k_scale : 1.f) * attn::kLog2e;
+  a.out_fp32 = out_fp32 != 0;
   int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.cnt_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (q8) {
@@ -536,16 +538,16 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* o,
-                float* lse, int B, int H_q, int H_kv, int max_len, int d, float scale, int dtype, void* workspace,
-                size_t workspace_bytes_given, void* stream) {
+                float* lse, int B, int H_q, int H_kv, int max_len, int d, float scale, int dtype, int out_fp32,
+                void* workspace, size_t workspace_bytes_given, void* stream) {
   return decode_common("attn_decode", false, q, k_cache, v_cache, nullptr, seq_lens, o, lse, B, H_q, H_kv, max_len,
-                       0, 0, d, scale, dtype, workspace, workspace_bytes_given, stream);
+                       0, 0, d, scale, dtype, out_fp32, workspace, workspace_bytes_given, stream);
 }
 
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
                       const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d, int block_size,
-                      int max_blocks_per_seq, int num_blocks, float scale, int dtype, void* workspace,
-                      size_t workspace_bytes_given, void* stream) {
+                      int max_blocks_per_seq, int num_blocks, float scale, int dtype, int out_fp32,
+                      void* workspace, size_t workspace_bytes_given, void* stream) {
   if (!block_table) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged: null block table");
   if (block_size != 16)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged: block_size must be 16 (got %d)", block_size);
@@ -554,14 +556,15 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, con
   if ((long long)max_blocks_per_seq * 16 > 0x7FFFFFFFLL)
     return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged: max_blocks_per_seq too large");
   return decode_common("attn_decode_paged", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q, H_kv,
-                       max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
-                       workspace_bytes_given, stream);
+                       max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, out_fp32,
+                       workspace, workspace_bytes_given, stream);
 }
 
 int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
                           const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d,
                           int block_size, int max_blocks_per_seq, int num_blocks, float scale, float k_scale,
-                          float v_scale, int dtype, void* workspace, size_t workspace_bytes_given, void* stream) {
+                          float v_scale, int dtype, int out_fp32, void* workspace, size_t workspace_bytes_given,
+                          void* stream) {
   if (!block_table) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_fp8: null block table");
   if (block_size != 16)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_fp8: block_size must be 16 (got %d)", block_size);
@@ -574,15 +577,15 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
   cq.k_scale = k_scale;
   cq.v_scale = v_scale;
   return decode_common("attn_decode_paged_fp8", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q,
-                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
-                       workspace_bytes_given, stream, cq);
+                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, out_fp32,
+                       workspace, workspace_bytes_given, stream, cq);
 }
 
 int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
                            const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d,
                            int block_size, int max_blocks_per_seq, int num_blocks, float scale,
-                           const float* k_scales, const float* v_scales, int dtype, void* workspace,
-                           size_t workspace_bytes_given, void* stream) {
+                           const float* k_scales, const float* v_scales, int dtype, int out_fp32,
+                           void* workspace, size_t workspace_bytes_given, void* stream) {
   if (!block_table) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_int8: null block table");
   if (block_size != 16)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_int8: block_size must be 16 (got %d)", block_size);
@@ -595,15 +598,15 @@ int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool
   cq.k_scales = k_scales;
   cq.v_scales = v_scales;
   return decode_common("attn_decode_paged_int8", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q,
-                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
-                       workspace_bytes_given, stream, cq);
+                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, out_fp32,
+                       workspace, workspace_bytes_given, stream, cq);
 }
 
 int attn_decode_paged_int4(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
                            const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d,
                            int block_size, int max_blocks_per_seq, int num_blocks, float scale,
-                           const float* k_scales, const float* v_scales, int dtype, void* workspace,
-                           size_t workspace_bytes_given, void* stream) {
+                           const float* k_scales, const float* v_scales, int dtype, int out_fp32,
+                           void* workspace, size_t workspace_bytes_given, void* stream) {
   if (!block_table) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_paged_int4: null block table");
   if (block_size != 16)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_paged_int4: block_size must be 16 (got %d)", block_size);
@@ -616,8 +619,8 @@ int attn_decode_paged_int4(const void* q, const void* k_pool, const void* v_pool
   cq.k_scales = k_scales;
   cq.v_scales = v_scales;
   return decode_common("attn_decode_paged_int4", true, q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q,
-                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, workspace,
-                       workspace_bytes_given, stream, cq);
+                       H_kv, max_blocks_per_seq * 16, max_blocks_per_seq, num_blocks, d, scale, dtype, out_fp32,
+                       workspace, workspace_bytes_given, stream, cq);
 }
 
 }  // extern "C"

@@ -384,9 +384,14 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     } else {
       row0 = ((size_t)c.b * a.H_kv + g) * a.capacity + (size_t)c.st * kDecStage;
     }
-    // contiguous: rows past the capacity (last stage only) read the last row instead
+    // contiguous: K rows past the capacity (last stage only) read the last row
+    // instead.  V rows past the sequence's length read its last row: their
+    // weights are 0, but a slot that was never written may hold a NaN or an
+    // infinity, and 0 times those is not 0 (K rows past the length are harmless:
+    // their scores are replaced by -inf).
     const int kr = PAGED ? col : min(col, a.capacity - 1 - c.st * kDecStage);
-    const int vr = PAGED ? (l >> 2) : min(l >> 2, a.capacity - 1 - c.st * kDecStage);
+    const int vlim = c.len - 1 - c.st * kDecStage;  // >= 0: stage st starts inside the sequence
+    const int vr = min(l >> 2, vlim);
     if constexpr (I4) {
       // 4-bit rows: the 8-bit assignment at half the bytes (D / 8 bytes of K and
       // of V per lane: one 16-byte load at d = 128, 8 bytes at d = 64)
@@ -410,7 +415,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       const uint8_t* ks_src = kp + (row0 + kr) * RB + 16 * grp;
 #pragma unroll
       for (int i = 0; i < NKL; ++i) S.k[i] = load_stream(ks_src + 64 * i);
-      const int lim = PAGED ? kDecStage - 1 : a.capacity - 1 - c.st * kDecStage;
+      const int lim = min(kDecStage - 1, vlim);
 #pragma unroll
       for (int i = 0; i < NVL; ++i) {
         const int r = min(l / (RB / 16) + i * (1024 / RB), lim);
@@ -422,8 +427,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       // the other half).  The stage's V rows are contiguous: instruction i of
       // lane l moves their bytes 16 l + 1024 i, so every V load covers whole
       // cache lines; the transposing reads from LDS regroup them.  Contiguous
-      // cache: rows past the capacity read the last row instead.
-      const int lim = PAGED ? kDecStage - 1 : a.capacity - 1 - c.st * kDecStage;
+      // cache: rows past the capacity read the last row instead; V rows past
+      // the sequence's length read its last row.
+      const int lim = min(kDecStage - 1, vlim);
       const uint32_t cb = 16 * (l % Gm::CH);
       const uint8_t* ks_src = kp + (row0 + kr) * ROWB + 16 * grp;
 #pragma unroll

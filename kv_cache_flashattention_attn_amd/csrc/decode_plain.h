@@ -31,6 +31,7 @@ struct DecodeArgs {
   int num_blocks;
   int s_max;            // splits per (b, h_q) the workspace holds
   float scale_log2;
+  int out_fp32;         // the output o is fp32 instead of T
 };
 
 // Length of sequence b, clamped to [0, capacity]; raises a flag when clamped.
@@ -141,6 +142,7 @@ struct MergeArgs {
   int s_max;
   int chunk;        // tokens per split (piece_cnt == nullptr)
   int G, n_hg;      // query heads per KV head, groups of 16 of them (piece_cnt != nullptr)
+  int out_fp32;     // o is fp32 (the result before its rounding to T)
 };
 
 // Combine the split partials of one (sequence, query head): one wave, lanes
@@ -203,7 +205,13 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int c = lane + 64 * j;
-    if (c < D) store_elem<T>(a.o, ((size_t)b * a.H_q + h) * D + c, acc[j] * inv);
+    if (c < D) {
+      const size_t i = ((size_t)b * a.H_q + h) * D + c;
+      if (a.out_fp32)
+        static_cast<float*>(a.o)[i] = acc[j] * inv;
+      else
+        store_elem<T>(a.o, i, acc[j] * inv);
+    }
   }
   if (a.lse != nullptr && lane == 0)
     a.lse[(size_t)b * a.H_q + h] = wsum > 0.f ? Mb + __logf(wsum) : kNegInf;

@@ -92,16 +92,16 @@ def test_decode_rejects_bad_arguments():
     L = _lib_or_skip()
     ws = L.attn_decode_workspace_bytes(2, 8, 64, 128)
     # workspace too small
-    assert L.attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 64, 128, 0.1, 2, FAKE, ws - 1, None) == 3
+    assert L.attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 64, 128, 0.1, 2, 0, FAKE, ws - 1, None) == 3
     # missing workspace
-    assert L.attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 64, 128, 0.1, 2, 0, ws, None) == 3
+    assert L.attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 64, 128, 0.1, 2, 0, 0, ws, None) == 3
     # null seq_lens
-    assert L.attn_decode(FAKE, FAKE, FAKE, 0, FAKE, 0, 2, 8, 2, 64, 128, 0.1, 2, FAKE, ws, None) == 1
+    assert L.attn_decode(FAKE, FAKE, FAKE, 0, FAKE, 0, 2, 8, 2, 64, 128, 0.1, 2, 0, FAKE, ws, None) == 1
     # paged: block size 32
-    assert L.attn_decode_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 128, 32, 4, 8, 0.1, 2,
+    assert L.attn_decode_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 2, 128, 32, 4, 8, 0.1, 2, 0,
                                FAKE, ws, None) == 2
     # paged: null table
-    assert L.attn_decode_paged(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, 2, 8, 2, 128, 16, 4, 8, 0.1, 2,
+    assert L.attn_decode_paged(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 0, 2, 8, 2, 128, 16, 4, 8, 0.1, 2, 0,
                                FAKE, ws, None) == 1
 
 
