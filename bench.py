@@ -352,9 +352,9 @@ def main() -> int:
         K.attn_prefill_paged(kd["q"], kd["k_pool"], kd["v_pool"], k_table, k_lens, causal=True,
                              scale=kcase.sm_scale, return_lse=True, out=k_out, lse=k_lse)
         rec(7)
-        K.kv_append_fp8(f_kp, f_vp, g["k_new"], g["v_new"], g_lens, g_table, 0.5, 0.5)
+        K.kv_append_fp8(f_kp, f_vp, g["k_new"], g["v_new"], g_lens, g_table, synth.FP8_K_SCALE, synth.FP8_V_SCALE)
         rec(8)
-        K.attn_decode_paged_fp8(g["q"], f_kp, f_vp, g_table, g_seq, k_scale=0.5, v_scale=0.5,
+        K.attn_decode_paged_fp8(g["q"], f_kp, f_vp, g_table, g_seq, k_scale=synth.FP8_K_SCALE, v_scale=synth.FP8_V_SCALE,
                                 scale=fcase.sm_scale, workspace=g_ws, out=f_out)
         rec(9)
         K.kv_append_int8(i_kp, i_vp, g["k_new"], g["v_new"], g_lens, g_table, i_ks, i_vs)
@@ -362,7 +362,8 @@ def main() -> int:
         K.attn_decode_paged_int8(g["q"], i_kp, i_vp, g_table, g_seq, i_ks, i_vs, scale=fcase.sm_scale,
                                  workspace=g_ws, out=i_out)
         rec(11)
-        K.attn_prefill_fp8(q8, k8, v8, causal=True, scale=pcase.sm_scale, q_scale=0.5, k_scale=0.25, v_scale=1.0,
+        K.attn_prefill_fp8(q8, k8, v8, causal=True, scale=pcase.sm_scale, q_scale=synth.FP8_Q_SCALE,
+                           k_scale=synth.FP8_K_SCALE, v_scale=synth.FP8_V_SCALE,
                            return_lse=True, workspace=f8_ws, out=o8, lse=lse8)
         rec(12)
         K.kv_append_int4(i4_kp, i4_vp, g["k_new"], g["v_new"], g_lens, g_table, i4_ks, i4_vs)

@@ -284,6 +284,23 @@ def chunk_flops(lens: np.ndarray, n_new: int, H_q: int, d: int, causal: bool = T
     return 4.0 * d * H_q * pairs
 
 
+def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform over the 254 finite OCP FP8 E4M3 codes: every byte but 0x7F and
+    0xFF (the two NaNs), i.e. both signs, all sixteen exponent fields (field 0
+    holds the subnormals) and every mantissa, up to +-448."""
+    c = rng.integers(0, 254, size=shape, dtype=np.uint8)
+    return (c + (c >= 0x7F).astype(np.uint8)).astype(np.uint8)
+
+
+# E4M3 scales that keep the full code range usable at the decode and prefill
+# tolerances: K values up to 448 / 64 = 7 (logits of order one against N(0,1)
+# queries at d = 128) and V values up to 448 / 256 = 1.75 (outputs of order
+# one, where a 16-bit output's storage rounding is below 1e-2).
+FP8_K_SCALE = 1.0 / 64
+FP8_V_SCALE = 1.0 / 256
+FP8_Q_SCALE = 1.0 / 64
+
+
 def fp8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
                       base: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
     """Inputs of one decode step over an 8-bit (OCP FP8 E4M3) paged cache.
@@ -291,21 +308,15 @@ def fp8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
     Lengths, block table, q and the new token's K/V rows (in ``case.dtype``) are
     those of ``decode_inputs(case, lens)`` (or of ``base``, a result of that
     call, passed to skip drawing it again).  The pools hold E4M3 codes (uint8)
-    drawn from ``SFC64(case.seed + 7000)``: for every cached token a random sign,
-    exponent field in [3, 8] and mantissa (magnitudes 2^-4 .. 3.75); slots that
-    hold no token carry code 0x00 in K and 0x7E (448, the largest value) in V.
+    drawn from ``SFC64(case.seed + 7000)``, uniform over every finite code
+    (``fp8_codes``), K's pool then V's; slots that hold no token carry code 0x7F
+    (NaN) in both, which a decode must never weigh.
     """
     out = dict(base) if base is not None else decode_inputs(case, lens=lens)
     lens = out["lens"]
     table = out["block_table"]
     nblk, Hk, bs, d = out["k_pool"].shape
     rng = make_rng(case.seed + 7000)
-
-    def codes(shape):
-        s = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
-        e = rng.integers(3, 9, size=shape, dtype=np.uint8) << 3
-        m = rng.integers(0, 8, size=shape, dtype=np.uint8)
-        return s | e | m
 
     # which (block, slot) pairs hold a cached token
     held = np.zeros((nblk, bs), dtype=bool)
@@ -315,8 +326,8 @@ def fp8_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
         fill = np.clip(L - BLOCK_SIZE * np.arange(nb), 0, BLOCK_SIZE)
         held[table[b, :nb]] = np.arange(bs)[None, :] < fill[:, None]
     mask = held[:, None, :, None]
-    kp = np.where(mask, codes((nblk, Hk, bs, d)), np.uint8(0x00)).astype(np.uint8)
-    vp = np.where(mask, codes((nblk, Hk, bs, d)), np.uint8(0x7E)).astype(np.uint8)
+    kp = np.where(mask, fp8_codes(rng, (nblk, Hk, bs, d)), np.uint8(0x7F)).astype(np.uint8)
+    vp = np.where(mask, fp8_codes(rng, (nblk, Hk, bs, d)), np.uint8(0x7F)).astype(np.uint8)
     out.update(k_pool=kp, v_pool=vp)
     return out
 
@@ -395,20 +406,12 @@ def int4_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
 
 def fp8_prefill_inputs(case: PrefillCase) -> Dict[str, np.ndarray]:
     """Q, K, V of ``case``'s shapes as OCP FP8 E4M3 codes (uint8), drawn from
-    ``SFC64(case.seed + 9000)`` in the order Q, K, V: a random sign, exponent
-    field and mantissa each; the exponent field is in [3, 8] for Q and K
-    (magnitudes 2^-4 .. 3.75) and in [3, 7] for V (2^-4 .. 1.875, about the
-    spread of standard-normal draws)."""
+    ``SFC64(case.seed + 9000)`` in the order Q, K, V, each uniform over every
+    finite code (``fp8_codes``: subnormals, all exponent fields, +-448)."""
     rng = make_rng(case.seed + 9000)
-
-    def codes(shape, e_hi):
-        sgn = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
-        e = rng.integers(3, e_hi + 1, size=shape, dtype=np.uint8) << 3
-        m = rng.integers(0, 8, size=shape, dtype=np.uint8)
-        return sgn | e | m
-
-    return {"q": codes((case.B, case.H_q, case.N, case.d), 8), "k": codes((case.B, case.H_kv, case.N, case.d), 8),
-            "v": codes((case.B, case.H_kv, case.N, case.d), 7)}
+    return {"q": fp8_codes(rng, (case.B, case.H_q, case.N, case.d)),
+            "k": fp8_codes(rng, (case.B, case.H_kv, case.N, case.d)),
+            "v": fp8_codes(rng, (case.B, case.H_kv, case.N, case.d))}
 
 
 def tiny_decode_steps(case: PrefillCase = TINY_PREFILL, steps: int = TINY_DECODE_STEPS):

@@ -80,3 +80,21 @@ def assert_lse_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "
     if finite.any():
         mx = float(np.abs(got[finite] - ref[finite]).max())
         assert mx <= LSE_ABS[dtype], f"{what}: max-abs {mx:.3e} > {LSE_ABS[dtype]:.0e}"
+
+
+def assert_stored_output(o16, o32, ref: np.ndarray, dtype: str, what: str = "O"):
+    """The acceptance rule for every output stored in a 16-bit type.
+
+    ``o32`` is the same call with the fp32-output option: its arithmetic must meet
+    the bar on its own (max-abs and mean-abs against the fp64 oracle); the stored
+    16-bit output ``o16`` must be exactly ``o32`` rounded to nearest-even; and
+    ``o16`` then lies within the bar of the oracle plus its own storage rounding
+    (half an ulp of the exact value) in each element.  Returns (max, mean) of the
+    fp32 output's error.
+    """
+    mx, mean = assert_close(values_of(o32), ref, dtype, what=f"{what} (fp32 output)")
+    import synth  # storage rounding of the fp32 result (input preparation code, no attention arithmetic)
+    assert np.array_equal(bits_of(o16), synth.to_storage(o32.detach().cpu().numpy(), dtype)), \
+        f"{what}: 16-bit output is not the round-to-nearest-even of the fp32 result"
+    assert_close(values_of(o16), ref, dtype, what=what, storage_slack=True)
+    return mx, mean

@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_close, assert_lse_close, bits_of, to_dev, to_dev_i32, values_of
+from helpers import assert_close, assert_lse_close, assert_stored_output, bits_of, to_dev, to_dev_i32, values_of
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -20,10 +20,14 @@ def K():
     return k
 
 
-def run_step(K, case, lens=None, heads=None):
-    """One append + attend step on the GPU and in the oracle; returns GPU (O, lse)."""
+def run_step(K, case, lens=None, heads=None, inp=None):
+    """One append + attend step on the GPU and in the oracle; returns GPU (O, lse).
+
+    16-bit outputs are checked with the stored-output rule: the same call with
+    the fp32 output meets the bar, and the stored output is its
+    round-to-nearest-even."""
     print(f"[decode] {case}", flush=True)
-    inp = synth.decode_inputs(case, lens=lens)
+    inp = synth.decode_inputs(case, lens=lens) if inp is None else inp
     dt = case.dtype
     lens_d = to_dev_i32(inp["lens"])
     seq_d = to_dev_i32(inp["lens"] + case.n_new)
@@ -33,11 +37,13 @@ def run_step(K, case, lens=None, heads=None):
         table = to_dev_i32(inp["block_table"])
         K.kv_append(kc, vc, kn, vn, lens_d, table)
         o, lse = K.attn_decode_paged(q, kc, vc, table, seq_d, scale=case.sm_scale, return_lse=True)
+        o32 = K.attn_decode_paged(q, kc, vc, table, seq_d, scale=case.sm_scale, out_fp32=True)
         ocache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
     else:
         kc, vc = to_dev(inp["k_cache"], dt), to_dev(inp["v_cache"], dt)
         K.kv_append(kc, vc, kn, vn, lens_d)
         o, lse = K.attn_decode(q, kc, vc, seq_d, scale=case.sm_scale, return_lse=True)
+        o32 = K.attn_decode(q, kc, vc, seq_d, scale=case.sm_scale, out_fp32=True)
         ocache = oracle.ContigCache(inp["k_cache"], inp["v_cache"])
     torch.cuda.synchronize()
     assert K.attn_device_error_flags() == 0
@@ -46,11 +52,15 @@ def run_step(K, case, lens=None, heads=None):
     # the append image, byte for byte (whole buffers, untouched sentinels included)
     assert bits_of(kc).tobytes() == ocache.k.tobytes(), "K cache image differs"
     assert bits_of(vc).tobytes() == ocache.v.tobytes(), "V cache image differs"
-    got_o, got_l = values_of(o), lse.cpu().numpy().astype(np.float64)
+    got_o, got_o32, got_l = o, o32, lse.cpu().numpy().astype(np.float64)
     if heads is not None:
         idx = tuple(np.array(heads).T)
-        got_o, Oref, got_l, Lref = got_o[idx], Oref[idx], got_l[idx], Lref[idx]
-    assert_close(got_o, Oref, dt)
+        got_o, got_o32, Oref, got_l, Lref = got_o[idx], got_o32[idx], Oref[idx], got_l[idx], Lref[idx]
+    if dt == "f32":
+        assert_close(values_of(got_o), Oref, dt)
+        assert torch.equal(got_o, got_o32)
+    else:
+        assert_stored_output(got_o, got_o32, Oref, dt)
     assert_lse_close(got_l, Lref, dt)
     return o, lse
 
@@ -101,6 +111,41 @@ def test_one_long_sequence_many_pieces(K, paged):
 @pytest.mark.parametrize("n_new", [3, 17])
 def test_multi_token_append(K, paged, n_new):
     run_step(K, case(paged, 4, 8, 4, 128, "bf16", 0, 90, 40 + n_new, n_new=n_new))
+
+
+# 16-bit patterns written into cache slots that hold no token
+NONFINITE = {"bf16": (0x7FC0, 0x7F80, 0xFF80), "f16": (0x7E00, 0x7C00, 0xFC00)}  # NaN, +inf, -inf
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_ignores_nonfinite_slots_past_the_length(K, paged, dtype, d):
+    """Slots at or past a sequence's length may hold anything: here K holds NaN
+    and V cycles through NaN, +inf and -inf.  None of it may reach O or lse (a
+    weight of 0 times a NaN or an infinity is not 0, so such rows must never be
+    multiplied at all)."""
+    lens = np.array([0, 1, 14, 15, 17, 31, 100, 255, 256], dtype=np.int32)
+    c = case(paged, len(lens), 8, 2, d, dtype, 0, 300, 200 + d)
+    inp = synth.decode_inputs(c, lens=lens)
+    nan, pinf, ninf = NONFINITE[dtype]
+    after = lens + c.n_new  # tokens held once the append has run
+    if paged:
+        kp, vp, table = inp["k_pool"], inp["v_pool"], inp["block_table"]
+        held = np.zeros(kp.shape[0] * 16, dtype=bool)
+        for b in range(c.B):
+            for t in range(int(after[b])):
+                held[table[b, t // 16] * 16 + t % 16] = True
+        empty = ~held.reshape(kp.shape[0], 1, 16, 1).repeat(c.H_kv, 1).repeat(d, 3)
+        kk, vv = kp, vp
+    else:
+        kk, vv = inp["k_cache"], inp["v_cache"]
+        empty = np.arange(kk.shape[2])[None, None, :, None] >= after[:, None, None, None]
+        empty = np.broadcast_to(empty, kk.shape)
+    pattern = np.array([nan, pinf, ninf], dtype=np.uint16)[np.arange(vv.size).reshape(vv.shape) % 3]
+    kk[empty] = nan
+    vv[empty] = pattern[empty]
+    run_step(K, c, inp=inp)
 
 
 def test_paged_identity_table_matches_contiguous(K):

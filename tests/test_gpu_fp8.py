@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_close, assert_lse_close, to_dev, to_dev_i32, values_of
+from helpers import assert_lse_close, assert_stored_output, to_dev, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -52,7 +52,10 @@ def test_fp8_append_image_is_bit_exact(K, dtype, scales):
     assert vp.cpu().numpy().tobytes() == cache.v.tobytes(), "V pool image differs"
 
 
-def run_fp8(K, case, lens=None, ks=0.5, vs=1.0, heads=None):
+def run_fp8(K, case, lens=None, ks=synth.FP8_K_SCALE, vs=synth.FP8_V_SCALE, heads=None):
+    """Append + decode over pools of every finite E4M3 code (empty slots hold NaN
+    codes), checked with the stored-output rule: the fp32-output call meets the
+    bar, the 16-bit output is its round-to-nearest-even."""
     print(f"[fp8] {case} k_scale={ks} v_scale={vs}", flush=True)
     inp = synth.fp8_decode_inputs(case, lens=lens)
     dt = case.dtype
@@ -61,20 +64,24 @@ def run_fp8(K, case, lens=None, ks=0.5, vs=1.0, heads=None):
     table = to_dev_i32(inp["block_table"])
     q = to_dev(inp["q"], dt)
     K.kv_append_fp8(kp, vp, to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt), lens_d, table, ks, vs)
-    o, lse = K.attn_decode_paged_fp8(q, kp, vp, table, to_dev_i32(inp["lens"] + 1), k_scale=ks, v_scale=vs,
-                                     scale=case.sm_scale, return_lse=True)
+    seq = to_dev_i32(inp["lens"] + 1)
+    o, lse = K.attn_decode_paged_fp8(q, kp, vp, table, seq, k_scale=ks, v_scale=vs, scale=case.sm_scale,
+                                     return_lse=True)
+    o32 = K.attn_decode_paged_fp8(q, kp, vp, table, seq, k_scale=ks, v_scale=vs, scale=case.sm_scale,
+                                  out_fp32=True)
     torch.cuda.synchronize()
     assert K.attn_device_error_flags() == 0
     cache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
     Oref, Lref = oracle.decode_step_fp8(cache, inp["q"], inp["k_new"], inp["v_new"], inp["lens"], case.sm_scale, dt,
                                         ks, vs, heads=heads)
     assert kp.cpu().numpy().tobytes() == cache.k.tobytes(), "K pool image differs"
-    got_o, got_l = values_of(o), lse.cpu().numpy().astype(np.float64)
+    got_l = lse.cpu().numpy().astype(np.float64)
     if heads is not None:
         idx = tuple(np.array(heads).T)
-        got_o, Oref, got_l, Lref = got_o[idx], Oref[idx], got_l[idx], Lref[idx]
-    assert_close(got_o, Oref, dt)
+        o, o32, Oref, got_l, Lref = o[idx], o32[idx], Oref[idx], got_l[idx], Lref[idx]
+    mx, mean = assert_stored_output(o, o32, Oref, dt)
     assert_lse_close(got_l, Lref, dt)
+    print(f"[fp8] fp32-output max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -86,15 +93,19 @@ def test_fp8_decode_chunk_boundaries(K, d, dtype):
 
 @pytest.mark.parametrize("G", [1, 4, 8, 16])
 def test_fp8_decode_gqa_groups(K, G):
-    run_fp8(K, synth.DecodeCase("fp8", 3, 2 * G, 2, 128, "bf16", 1, 700, True, 120 + G), ks=1.0, vs=1.0)
+    run_fp8(K, synth.DecodeCase("fp8", 3, 2 * G, 2, 128, "bf16", 1, 700, True, 120 + G))
 
 
-def test_fp8_decode_workload_sampled_heads(K):
-    """The paged decode workload (B=64, H_q=32, H_kv=8, lengths 128 .. 8192) with an 8-bit cache."""
-    c = synth.DECODE_PAGED
-    r = np.random.Generator(np.random.SFC64(322))
-    heads = sorted({(int(b), int(h)) for b, h in zip(r.integers(0, c.B, 40), r.integers(0, c.H_q, 40))})
-    run_fp8(K, c, ks=0.25, vs=0.5, heads=heads)
+def test_fp8_decode_workload(K):
+    """The paged decode workload (B=64, H_q=32, H_kv=8, lengths 128 .. 8192) with an
+    8-bit cache, every (sequence, head)."""
+    run_fp8(K, synth.DECODE_PAGED)
+
+
+def test_fp8_decode_other_scales(K):
+    """Scales that are not powers of two (the append's fp32 reciprocal and the
+    decode's scaling paths)."""
+    run_fp8(K, synth.DecodeCase("fp8", 4, 8, 2, 128, "bf16", 1, 400, True, 140), ks=0.0123, vs=0.0031)
 
 
 def test_fp8_bad_block_raises_flag(K):

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_close, assert_lse_close, to_dev, to_dev_i32, values_of
+from helpers import assert_lse_close, assert_stored_output, to_dev, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -72,19 +72,20 @@ def run_int8(K, case, lens=None, heads=None):
     table = to_dev_i32(inp["block_table"])
     q = to_dev(inp["q"], dt)
     K.kv_append_int8(kp, vp, to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt), lens_d, table, ks, vs)
-    o, lse = K.attn_decode_paged_int8(q, kp, vp, table, to_dev_i32(inp["lens"] + 1), ks, vs, scale=case.sm_scale,
-                                      return_lse=True)
+    seq = to_dev_i32(inp["lens"] + 1)
+    o, lse = K.attn_decode_paged_int8(q, kp, vp, table, seq, ks, vs, scale=case.sm_scale, return_lse=True)
+    o32 = K.attn_decode_paged_int8(q, kp, vp, table, seq, ks, vs, scale=case.sm_scale, out_fp32=True)
     torch.cuda.synchronize()
     assert K.attn_device_error_flags() == 0
     cache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
     Oref, Lref = oracle.decode_step_int8(cache, inp["q"], inp["k_new"], inp["v_new"], inp["lens"], case.sm_scale, dt,
                                          inp["k_scales"], inp["v_scales"], heads=heads)
     assert kp.cpu().numpy().tobytes() == cache.k.tobytes(), "K pool image differs"
-    got_o, got_l = values_of(o), lse.cpu().numpy().astype(np.float64)
+    got_l = lse.cpu().numpy().astype(np.float64)
     if heads is not None:
         idx = tuple(np.array(heads).T)
-        got_o, Oref, got_l, Lref = got_o[idx], Oref[idx], got_l[idx], Lref[idx]
-    assert_close(got_o, Oref, dt)
+        o, o32, Oref, got_l, Lref = o[idx], o32[idx], Oref[idx], got_l[idx], Lref[idx]
+    assert_stored_output(o, o32, Oref, dt)
     assert_lse_close(got_l, Lref, dt)
 
 
@@ -100,12 +101,10 @@ def test_int8_decode_gqa_groups(K, G):
     run_int8(K, synth.DecodeCase("i8", 3, 2 * G, 2, 128, "bf16", 1, 700, True, 220 + G))
 
 
-def test_int8_decode_workload_sampled_heads(K):
-    """The paged decode workload (B=64, H_q=32, H_kv=8, lengths 128 .. 8192) with an int8 cache."""
-    c = synth.DECODE_PAGED
-    r = np.random.Generator(np.random.SFC64(422))
-    heads = sorted({(int(b), int(h)) for b, h in zip(r.integers(0, c.B, 40), r.integers(0, c.H_q, 40))})
-    run_int8(K, c, heads=heads)
+def test_int8_decode_workload(K):
+    """The paged decode workload (B=64, H_q=32, H_kv=8, lengths 128 .. 8192) with an
+    int8 cache, every (sequence, head)."""
+    run_int8(K, synth.DECODE_PAGED)
 
 
 def test_int8_bad_block_raises_flag(K):
@@ -164,19 +163,20 @@ def run_int4(K, case, lens=None, heads=None):
     table = to_dev_i32(inp["block_table"])
     q = to_dev(inp["q"], dt)
     K.kv_append_int4(kp, vp, to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt), lens_d, table, ks, vs)
-    o, lse = K.attn_decode_paged_int4(q, kp, vp, table, to_dev_i32(inp["lens"] + 1), ks, vs, scale=case.sm_scale,
-                                      return_lse=True)
+    seq = to_dev_i32(inp["lens"] + 1)
+    o, lse = K.attn_decode_paged_int4(q, kp, vp, table, seq, ks, vs, scale=case.sm_scale, return_lse=True)
+    o32 = K.attn_decode_paged_int4(q, kp, vp, table, seq, ks, vs, scale=case.sm_scale, out_fp32=True)
     torch.cuda.synchronize()
     assert K.attn_device_error_flags() == 0
     cache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
     Oref, Lref = oracle.decode_step_int4(cache, inp["q"], inp["k_new"], inp["v_new"], inp["lens"], case.sm_scale, dt,
                                          inp["k_scales"], inp["v_scales"], heads=heads)
     assert kp.cpu().numpy().tobytes() == cache.k.tobytes(), "K pool image differs"
-    got_o, got_l = values_of(o), lse.cpu().numpy().astype(np.float64)
+    got_l = lse.cpu().numpy().astype(np.float64)
     if heads is not None:
         idx = tuple(np.array(heads).T)
-        got_o, Oref, got_l, Lref = got_o[idx], Oref[idx], got_l[idx], Lref[idx]
-    assert_close(got_o, Oref, dt)
+        o, o32, Oref, got_l, Lref = o[idx], o32[idx], Oref[idx], got_l[idx], Lref[idx]
+    assert_stored_output(o, o32, Oref, dt)
     assert_lse_close(got_l, Lref, dt)
 
 
@@ -192,12 +192,10 @@ def test_int4_decode_gqa_groups(K, G):
     run_int4(K, synth.DecodeCase("i4", 3, 2 * G, 2, 128, "bf16", 1, 700, True, 260 + G))
 
 
-def test_int4_decode_workload_sampled_heads(K):
-    """The paged decode workload (B=64, H_q=32, H_kv=8, lengths 128 .. 8192) with an int4 cache."""
-    c = synth.DECODE_PAGED
-    r = np.random.Generator(np.random.SFC64(433))
-    heads = sorted({(int(b), int(h)) for b, h in zip(r.integers(0, c.B, 40), r.integers(0, c.H_q, 40))})
-    run_int4(K, c, heads=heads)
+def test_int4_decode_workload(K):
+    """The paged decode workload (B=64, H_q=32, H_kv=8, lengths 128 .. 8192) with an
+    int4 cache, every (sequence, head)."""
+    run_int4(K, synth.DECODE_PAGED)
 
 
 def test_int4_bad_block_raises_flag(K):

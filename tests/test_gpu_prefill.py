@@ -76,6 +76,16 @@ def test_gqa_small_noncausal_d64(K, dtype):
     run_case(K, 3201, 1, 4, 1, 1000, 64, dtype, False)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,H_q,H_kv,N", [(1, 17, 17, 1900), (1, 16, 4, 2000), (2, 16, 4, 1100)])
+def test_noncausal_d64_on_both_sides_of_the_kernel_switch(K, dtype, B, H_q, H_kv, N):
+    """Non-causal d = 64 problems with fewer 128-row query blocks than the GPU has
+    compute units (256) take the key-split kernel; the others take the main MFMA
+    kernel.  Block counts here: 255 (key-split), 256 and 288 (main kernel), with
+    GQA and ragged lengths."""
+    run_case(K, 3300 + N + H_q, B, H_q, H_kv, N, 64, dtype, False)
+
+
 def test_fp32_output_mode(K):
     """fp32 output separates arithmetic error from bf16 storage rounding."""
     o = run_case(K, 4000, 1, 4, 4, 513, 128, "bf16", True, out_fp32=True)

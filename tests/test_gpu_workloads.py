@@ -1,9 +1,8 @@
 """The five workloads at full size: GPU vs the fp64 oracle.
 
-Small workloads are compared element by element; the large ones on sampled
-rows / heads that the oracle computes one by one, plus properties that hold at
-any size (finite outputs; every output row is a convex combination of value
-rows, so it lies inside their per-component range).
+Every workload is compared element by element: every output row of the
+prefills (O and lse) and every (sequence, head) of the decodes, and the whole
+byte image of each cache after the append.
 """
 import numpy as np
 import pytest
@@ -87,52 +86,37 @@ def test_f16_prefill_1x8x1024x64(K):
     assert_lse_close(lse.cpu().numpy().astype(np.float64), Lref, c.dtype)
 
 
-def _convex_hull_check(O, V, G):
-    """Every O row of head h lies inside [min, max] of its KV head's value rows, per component."""
-    vmin = V.amin(dim=2).repeat_interleave(G, dim=1)  # [B, H_q, d]
-    vmax = V.amax(dim=2).repeat_interleave(G, dim=1)
-    Of = O.float()
-    tol = 1e-2
-    assert bool(torch.all(Of >= vmin.float().unsqueeze(2) - tol))
-    assert bool(torch.all(Of <= vmax.float().unsqueeze(2) + tol))
-
-
 def test_bf16_causal_prefill_4x32x4096x128(K):
+    """Every output row (O and lse) of the causal workload against the fp64
+    oracle, one (batch, head) at a time."""
     c = synth.PREFILL_BF16_CAUSAL
     print(f"[workload] {c.name}", flush=True)
     raw = synth.prefill_inputs(c)
     q, k, v = (to_dev(raw[n], c.dtype) for n in ("q", "k", "v"))
     o, lse = K.attn_prefill(q, k, v, causal=True, scale=c.sm_scale, return_lse=True)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
-    _convex_hull_check(o, v, 1)
-    r = np.random.Generator(np.random.SFC64(123))
-    rows = []
-    for b in range(c.B):
-        for h in r.choice(c.H_q, 4, replace=False):
-            for i in [0, 1, 63, 64, 127, 128, 129, 2047, 2048, c.N - 1] + list(r.integers(0, c.N, 6)):
-                rows.append((b, int(h), int(i)))
-    Oref, Lref = oracle.attention_rows(_Lazy(raw["q"], c.dtype), _Lazy(raw["k"], c.dtype),
-                                       _Lazy(raw["v"], c.dtype), c.sm_scale, rows, causal=True)
-    og = values_of(o)
+    assert K.attn_device_error_flags() == 0
+    og = bits_of(o)
     lg = lse.cpu().numpy().astype(np.float64)
-    got = np.stack([og[b, h, i] for b, h, i in rows])
-    gotl = np.array([lg[b, h, i] for b, h, i in rows])
-    assert_close(got, Oref, c.dtype)
-    assert_lse_close(gotl, Lref, c.dtype)
+    del o, lse, q, k, v
+    mx, total, lmx = 0.0, 0.0, 0.0
+    for b in range(c.B):
+        for h in range(c.H_q):
+            Q, Kk, V = (oracle.decode_bits(raw[n][b:b + 1, h:h + 1], c.dtype) for n in ("q", "k", "v"))
+            Oref, Lref = oracle.one_shot(Q, Kk, V, c.sm_scale, causal=True)
+            err = np.abs(oracle.decode_bits(og[b:b + 1, h:h + 1], c.dtype) - Oref)
+            assert np.all(np.isfinite(err)), f"non-finite output at (b, h) = ({b}, {h})"
+            assert float(err.max()) <= 1e-2, f"(b, h) = ({b}, {h}): max-abs {float(err.max()):.3e}"
+            mx, total = max(mx, float(err.max())), total + float(err.sum())
+            lmx = max(lmx, float(np.abs(lg[b:b + 1, h:h + 1] - Lref).max()))
+    mean = total / og.size
+    print(f"[workload] {c.name}: all {og.size // c.d} rows, O max-abs {mx:.3e} mean-abs {mean:.3e}, "
+          f"lse max-abs {lmx:.3e}", flush=True)
+    assert mean <= 1e-3, f"O mean-abs {mean:.3e}"
+    assert lmx <= 1e-3, f"lse max-abs {lmx:.3e}"
 
 
-class _Lazy:
-    """Decodes storage bits to fp64 on slicing (so the oracle never holds the whole tensor)."""
-
-    def __init__(self, bits, dtype):
-        self.bits, self.dtype, self.shape = bits, dtype, bits.shape
-
-    def __getitem__(self, idx):
-        return oracle.decode_bits(self.bits[idx], self.dtype)
-
-
-def _decode_workload(K, c, n_heads=24):
+def _decode_workload(K, c):
     print(f"[workload] {c.name}", flush=True)
     inp = synth.decode_inputs(c)
     dt = c.dtype
@@ -151,15 +135,13 @@ def _decode_workload(K, c, n_heads=24):
         ocache = oracle.ContigCache(inp["k_cache"], inp["v_cache"])
     torch.cuda.synchronize()
     assert K.attn_device_error_flags() == 0
-    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
-    r = np.random.Generator(np.random.SFC64(321))
-    bs = {int(np.argmin(lens)), int(np.argmax(lens))} | set(int(x) for x in r.choice(c.B, 6, replace=False))
-    heads = sorted({(b, int(h)) for b in bs for h in r.choice(c.H_q, max(1, n_heads // len(bs)), replace=False)})
-    Oref, Lref = oracle.decode_step(ocache, inp["q"], inp["k_new"], inp["v_new"], lens, c.sm_scale, dt,
-                                    heads=heads)
-    idx = tuple(np.array(heads).T)
-    assert_close(values_of(o)[idx], Oref[idx], dt)
-    assert_lse_close(lse.cpu().numpy().astype(np.float64)[idx], Lref[idx], dt)
+    # every (sequence, head) against the oracle
+    Oref, Lref = oracle.decode_step(ocache, inp["q"], inp["k_new"], inp["v_new"], lens, c.sm_scale, dt)
+    mx, mean = assert_close(values_of(o), Oref, dt)
+    lg = lse.cpu().numpy().astype(np.float64)
+    assert_lse_close(lg, Lref, dt)
+    print(f"[workload] {c.name}: all {c.B * c.H_q} heads, O max-abs {mx:.3e} mean-abs {mean:.3e}, "
+          f"lse max-abs {float(np.abs(lg - Lref).max()):.3e}", flush=True)
     # whole-buffer append images
     assert np.array_equal(bits_of(kc), ocache.k), "K cache image differs"
     assert np.array_equal(bits_of(vc), ocache.v), "V cache image differs"
