@@ -33,20 +33,35 @@ def command(out: str = LIB_PATH, extra=()) -> list:
     ]
 
 
+ASM_PATH = os.path.join(PKG_DIR, "libattn_gfx950.s")  # device assembly, for hazard_scan
+
+
+def asm_command(out: str = ASM_PATH) -> list:
+    """The same device code as the library, as gfx950 assembly text."""
+    cmd = command(out)
+    cmd.remove("-shared")
+    cmd.remove("-fPIC")
+    return cmd[:1] + ["--cuda-device-only", "-S"] + cmd[1:]
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libattn.so (always; never reuses a stale library). Returns its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = command(tmp)
+    """Compile libattn.so (always; never reuses a stale library) and, alongside, the
+    device assembly that tests/test_build_hazards.py checks. Returns the library path."""
+    tmp, tmp_asm = LIB_PATH + ".tmp", ASM_PATH + ".tmp"
+    cmd, acmd = command(tmp), asm_command(tmp_asm)
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = [ln for ln in (r.stderr or "").splitlines()
-             if "packed-fp32-ops" not in ln or "error" in ln]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(noise))
-    if verbose and noise:
-        print("\n".join(noise), file=sys.stderr)
+    procs = [subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True) for c in (cmd, acmd)]
+    results = [(p.wait(), p.communicate()[1]) for p in procs]
+    for (rc, err), what in zip(results, ("library", "assembly")):
+        noise = [ln for ln in (err or "").splitlines()
+                 if ("packed-fp32-ops" not in ln and "hip-link" not in ln) or "error" in ln]
+        if rc != 0:
+            raise RuntimeError(f"hipcc ({what}) failed:\n" + "\n".join(noise))
+        if verbose and noise and what == "library":
+            print("\n".join(noise), file=sys.stderr)
     os.replace(tmp, LIB_PATH)
+    os.replace(tmp_asm, ASM_PATH)
     return LIB_PATH
 
 

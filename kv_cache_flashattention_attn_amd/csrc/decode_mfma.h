@@ -495,9 +495,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   auto compute = [&](const Cursor& c, const Stage& S, const bool last) {
     if (!S.ok && l == 0) raise_device_error(2);
     if (S.qnew) {
-      // New segment: clear the running state and O (explicitly: measured on
-      // this part, relying on the first stage's rescale by exp2(-inf) = 0 to
-      // clear O left a previous segment's accumulator in place in some builds).
+      // New segment: clear the running state and O.
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = S.q[ks];
       if constexpr (QS) {
@@ -577,11 +575,14 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) sacc = mfma16k32<T>(S.k[ks], qf[ks], sacc);
     }
-    if (!S.ok || t0 + kDecStage > c.len) {
+    // Mask without a branch: the S^T accumulator is read right after the MFMA
+    // that writes it, and the wait states that read needs are only inserted
+    // reliably within one basic block.  A branch here once let the row maximum
+    // read a stale accumulator register on one path (a segment's non-final
+    // stages): the reference maximum of a column then came from stale data, and
+    // at a segment start the O accumulator was not cleared for that column.
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!S.ok || t0 + 4 * grp + i >= c.len) sacc[i] = kNegInf;
-    }
+    for (int i = 0; i < 4; ++i) sacc[i] = (S.ok && t0 + 4 * grp + i < c.len) ? sacc[i] : kNegInf;
     float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     tmax = fmaxf(tmax, xor_shfl(tmax, 16));
     tmax = max_pair32(tmax);
