@@ -195,6 +195,31 @@ int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
                        int dtype, void* stream);
 
 /*
+ * attn_decode_paged_noalloc -- attn_decode_paged with no workspace argument and
+ * no allocation of any kind.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The workspace is a
+ * 64 MiB static device array inside the library (one per GPU, held until the
+ * process ends); its address is looked up once per device, on the first call
+ * there.  Arguments, layouts, results and errors are those of
+ * attn_decode_paged; the workspace it would need,
+ * attn_decode_workspace_bytes(B, H_q, max_blocks_per_seq * 16, d), must fit in
+ * the 64 MiB (e.g. B = 64, H_q = 32, d = 128 and 8,208 tokens of capacity need
+ * about 37 MB), else ATTN_ERR_WORKSPACE and nothing is launched.
+ * Every call on a GPU uses the same array: calls that overlap in time on one
+ * GPU (different streams, or other host threads) race and must not be issued;
+ * calls in one stream are ordered and safe.  Nothing in the array has to start
+ * at zero: every part a call reads was written earlier in the same call.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* o, float* lse,
+                              int B, int H_q, int H_kv, int d, int block_size,
+                              int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                              int out_fp32, void* stream);
+
+/*
  * kv_append_int4 / attn_decode_paged_int4 -- the int8 cache's scheme at 4 bits.
  *
  * Same per-channel scales and rounding as kv_append_int8 with codes clamped to

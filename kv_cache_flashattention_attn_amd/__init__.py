@@ -26,7 +26,7 @@ __all__ = [
     "AttnError", "lib", "lib_path", "attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode",
     "attn_decode_paged", "kv_append_fp8", "attn_decode_paged_fp8", "kv_append_int8", "attn_decode_paged_int8",
     "kv_copy_blocks", "attn_prefill_fp8", "attn_prefill_fp8_workspace_bytes", "kv_append_int4",
-    "attn_decode_paged_int4",
+    "attn_decode_paged_int4", "attn_decode_paged_noalloc",
     "attn_decode_workspace_bytes", "attn_device_error_flags", "attn_version", "DTYPE_CODES",
     "EXPORTED_SYMBOLS",
 ]
@@ -41,7 +41,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3:
 EXPORTED_SYMBOLS = ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
                     "kv_append_fp8", "attn_decode_paged_fp8", "kv_append_int8", "attn_decode_paged_int8",
                     "kv_copy_blocks", "attn_prefill_fp8", "attn_prefill_fp8_workspace_bytes", "kv_append_int4",
-                    "attn_decode_paged_int4",
+                    "attn_decode_paged_int4", "attn_decode_paged_noalloc",
                     "attn_decode_workspace_bytes", "attn_last_error", "attn_version",
                     "attn_device_error_flags",
                     "attn_block_pool_create", "attn_block_pool_destroy", "attn_block_pool_free_blocks",
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                     i32, vp, sz, vp]
+    L.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                            i32, vp]
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_last_error.restype = ctypes.c_char_p
@@ -106,7 +108,7 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_prefill", "attn_prefill_paged", "kv_append", "attn_decode", "attn_decode_paged",
                  "kv_append_fp8", "attn_decode_paged_fp8", "attn_device_error_flags", "kv_copy_blocks",
                  "kv_append_int8", "attn_decode_paged_int8", "attn_prefill_fp8", "kv_append_int4",
-                 "attn_decode_paged_int4",
+                 "attn_decode_paged_int4", "attn_decode_paged_noalloc",
                  "attn_block_pool_free_blocks", "attn_block_pool_holders", "attn_block_pool_reserve",
                  "attn_block_pool_reserve_batch", "attn_block_pool_release", "attn_block_pool_fork"):
         getattr(L, name).restype = i32
@@ -272,6 +274,29 @@ def attn_decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
                                  _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                  _stream())
     _check("attn_decode_paged", rc)
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_paged_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor, scale: Optional[float] = None,
+                              return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, out_fp32: bool = False):
+    """attn_decode_paged with the library's static workspace (no workspace argument,
+    no allocation in the library; pass ``out`` and ``lse`` to allocate nothing here either)."""
+    B, H_q, d = q.shape
+    nb, H_kv, bs, _ = k_pool.shape
+    mbps = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = _out(q, q.shape, out_fp32) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    rc = lib().attn_decode_paged_noalloc(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                         _dev(block_table, "block_table", torch.int32),
+                                         _dev(seq_lens, "seq_lens", torch.int32), _dev(out, "out"),
+                                         _dev(lse, "lse", torch.float32) if return_lse else 0,
+                                         B, H_q, H_kv, d, bs, mbps, nb, scale, _code(q), int(bool(out_fp32)),
+                                         _stream())
+    _check("attn_decode_paged_noalloc", rc)
     return (out, lse) if return_lse else out
 
 

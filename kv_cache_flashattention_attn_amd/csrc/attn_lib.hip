@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -313,6 +314,35 @@ int decode_q8_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, co
   if (cq.kind == attn::kKVFp8) return decode_q8_typed<T, attn::kKVFp8>(a, o, lse, d, cq, cnt, st);
   if (cq.kind == attn::kKVInt4) return decode_q8_typed<T, attn::kKVInt4>(a, o, lse, d, cq, cnt, st);
   return decode_q8_typed<T, attn::kKVInt8>(a, o, lse, d, cq, cnt, st);
+}
+
+// Workspace of attn_decode_paged_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it is a stand-in, not a device address): it
+// uses the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
 }
 
 int check_decode_common(const char* fn, const void* q, const void* k, const void* v, const int32_t* lens,
@@ -844,6 +874,26 @@ int attn_block_pool_fork(attn_block_pool* pool, const int32_t* src, int32_t* dst
 }
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                              const int32_t* seq_lens, void* o, float* lse, int B, int H_q, int H_kv, int d,
+                              int block_size, int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                              int out_fp32, void* stream) {
+  const char* fn = "attn_decode_paged_noalloc";
+  // sizes that attn_decode_paged would reject are left to its own checks
+  if (B >= 1 && H_q >= 1 && d >= 1 && max_blocks_per_seq >= 1 && (long long)max_blocks_per_seq * 16 <= 0x7FFFFFFFLL) {
+    const size_t need = workspace_bytes(B, H_q, max_blocks_per_seq * 16, d);
+    if (need > kScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE,
+                  "%s: B=%d, H_q=%d, max_blocks_per_seq=%d, d=%d need %zu bytes of workspace; the library's "
+                  "static scratch holds %zu (use attn_decode_paged with a caller workspace instead)",
+                  fn, B, H_q, max_blocks_per_seq, d, need, kScratchBytes);
+  }
+  void* ws = scratch_address();
+  if (!ws) return fail(ATTN_ERR_HIP, "%s: the address of the static scratch could not be obtained", fn);
+  return attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H_q, H_kv, d, block_size,
+                           max_blocks_per_seq, num_blocks, scale, dtype, out_fp32, ws, kScratchBytes, stream);
+}
 
 const char* attn_version(void) { return "libattn 0.1.0 (gfx950)"; }
 

@@ -134,3 +134,15 @@ def test_prefill_paged_rejects_bad_arguments(args, code):
     L = _lib_or_skip()
     assert L.attn_prefill_paged(*args, None) == code
     assert L.attn_last_error()
+
+
+def test_noalloc_decode_refuses_a_workspace_beyond_its_static_array():
+    """The allocation-free paged decode checks its workspace need against the
+    library's static array before anything else: nothing is launched."""
+    L = _lib_or_skip()
+    # B = 32, H_q = 64, 32,784 tokens of capacity at d = 128: about 136 MB > 64 MiB
+    rc = L.attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 64, 8, 128, 16, 2049, 40000,
+                                     0.088, 2, 0, None)
+    assert rc == 3
+    msg = L.attn_last_error().decode()
+    assert "static scratch" in msg and str(64 << 20) in msg
