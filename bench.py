@@ -93,6 +93,26 @@ def blas_threads() -> int:
         return 1
 
 
+def host_info() -> dict:
+    """The host the oracle ran on: CPU model, cores this process may run on
+    (sched_getaffinity), and the BLAS threads the oracle's matrix products used
+    (its elementwise work is single-threaded)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "affinity_cores": affinity, "blas_threads": blas_threads()}
+
+
 def block_pool_leg() -> dict:
     """Host side of the paged cache: the serving simulation on the chat workload
     (contiguous max_len reservations vs 16-token blocks from the native pool)
@@ -188,9 +208,10 @@ def cpu_baseline(seconds: float, prefill_case, prefill_raw, paged_case, paged_in
         flops += 4.0 * c.d * c.N * (c.N + 1) / 2
         heads += 1
     dt = time.perf_counter() - t0
-    out["prefill"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+    host = host_info()
+    out["prefill"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host["blas_threads"], "kind": "oracle",
                       "sample": f"{heads} of {c.B * c.H_q} (batch, head) pairs of the causal prefill, "
-                                f"one_shot in fp64, {dt:.1f} s"}
+                                f"one_shot in fp64, {dt:.1f} s", "host": host}
     # decode: whole sequences of the paged workload (append + gather + attend)
     t0 = time.perf_counter()
     nbytes = 0
@@ -207,9 +228,10 @@ def cpu_baseline(seconds: float, prefill_case, prefill_raw, paged_case, paged_in
         nbytes += (int(paged_inp["lens"][b]) + pc.n_new) * pc.H_kv * pc.d * 2 * 2
         seqs += 1
     dt = time.perf_counter() - t0
-    out["decode"] = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+    out["decode"] = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": host["blas_threads"], "kind": "oracle",
                      "sample": f"{seqs} of {pc.B} sequences of the paged decode (append, gather, attend "
-                               f"all {pc.H_q} query heads) in fp64, {dt:.1f} s (+{copy_s:.1f} s pool copy)"}
+                               f"all {pc.H_q} query heads) in fp64, {dt:.1f} s (+{copy_s:.1f} s pool copy)",
+                     "host": host}
     return out
 
 
@@ -352,10 +374,11 @@ def main() -> int:
         K.attn_prefill_paged(kd["q"], kd["k_pool"], kd["v_pool"], k_table, k_lens, causal=True,
                              scale=kcase.sm_scale, return_lse=True, out=k_out, lse=k_lse)
         rec(7)
-        K.kv_append_fp8(f_kp, f_vp, g["k_new"], g["v_new"], g_lens, g_table, synth.FP8_K_SCALE, synth.FP8_V_SCALE)
+        K.kv_append_fp8(f_kp, f_vp, g["k_new"], g["v_new"], g_lens, g_table, synth.FP8_K_SCALE,
+                        synth.FP8_V_SCALE)
         rec(8)
-        K.attn_decode_paged_fp8(g["q"], f_kp, f_vp, g_table, g_seq, k_scale=synth.FP8_K_SCALE, v_scale=synth.FP8_V_SCALE,
-                                scale=fcase.sm_scale, workspace=g_ws, out=f_out)
+        K.attn_decode_paged_fp8(g["q"], f_kp, f_vp, g_table, g_seq, k_scale=synth.FP8_K_SCALE,
+                                v_scale=synth.FP8_V_SCALE, scale=fcase.sm_scale, workspace=g_ws, out=f_out)
         rec(9)
         K.kv_append_int8(i_kp, i_vp, g["k_new"], g["v_new"], g_lens, g_table, i_ks, i_vs)
         rec(10)

@@ -65,5 +65,23 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+ASAN_LIB_PATH = os.path.join(PKG_DIR, "libattn_asan.so")
+
+
+def build_asan(verbose: bool = False) -> str:
+    """A host-AddressSanitizer build of the library (host code only; the device code
+    is the ordinary one), for the block pool's and the argument checks' CPU tests:
+    tests/run_asan.py loads it with the sanitizer runtime preloaded."""
+    cmd = command(ASAN_LIB_PATH + ".tmp", extra=("-g", "-Xarch_host", "-fsanitize=address",
+                                                  "-Xarch_host", "-fno-omit-frame-pointer"))
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc (asan) failed:\n" + (r.stderr or ""))
+    os.replace(ASAN_LIB_PATH + ".tmp", ASAN_LIB_PATH)
+    return ASAN_LIB_PATH
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_asan(verbose=True) if "--asan" in sys.argv else build(verbose=True))
