@@ -146,75 +146,96 @@ struct MergeArgs {
 };
 
 // Combine the split partials of one (sequence, query head): one wave, lanes
-// across d.  The weights exp(lse_s - max lse) of 64 splits are computed at
-// once (lane s holds split s) and broadcast with v_readlane; the partial rows
-// of 16 splits are loaded before any is used, so they are in flight together.
+// across d (PER consecutive channels each).  A chunk of up to 64 splits is
+// weighted at once (lane s holds split s; the weights are broadcast with
+// v_readlane), and the partial rows of BATCH splits are loaded before any is
+// used.  The merge is latency-bound, so the loads are ordered for the fewest
+// round trips: the length and the piece count together, then a chunk's lse
+// values together with the rows of its first batch.  A chunk whose largest lse
+// exceeds the running maximum rescales what was summed before it (the tiles'
+// identity again), so the common case of at most 64 splits reads every lse once.
 template <typename T, int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(MergeArgs a) {
-  constexpr int PER = (D + 63) / 64;  // output components per lane
+  constexpr int PER = D >= 64 ? D / 64 : 1;  // consecutive output channels per lane
+  constexpr int BATCH = 16;                  // splits whose rows are in flight together
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
+  const int gh = a.piece_cnt == nullptr ? 0 : (h / a.G) * a.n_hg + (h % a.G) / 16;  // segment of this head
   int len = a.seq_lens[b];
+  const int pc = a.piece_cnt == nullptr ? 0 : a.piece_cnt[(size_t)b * a.H_q + gh];
   len = len < 0 ? 0 : (len > a.capacity ? a.capacity : len);
   int ns;
-  if (a.piece_cnt == nullptr) {
+  if (a.piece_cnt == nullptr)
     ns = (len + a.chunk - 1) / a.chunk;
-  } else {
-    const int gh = (h / a.G) * a.n_hg + (h % a.G) / 16;  // segment of this query head
-    ns = len == 0 ? 0 : a.piece_cnt[(size_t)b * a.H_q + gh];
-    ns = ns < 0 ? 0 : (ns > a.s_max ? a.s_max : ns);
-  }
+  else
+    ns = len == 0 ? 0 : (pc < 0 ? 0 : (pc > a.s_max ? a.s_max : pc));
   const size_t base = ((size_t)b * a.H_q + h) * a.s_max;
-  float M = kNegInf;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.part_lse[base + s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, xor_shfl(M, off));
-  const float Mb = M == kNegInf ? 0.f : M;
-  float wsum = 0.f;
-  for (int s = lane; s < ns; s += 64) wsum += fast_exp2((a.part_lse[base + s] - Mb) * kLog2e);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) wsum += xor_shfl(wsum, off);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-
-  float acc[PER];
+  const int c0 = lane * PER;  // first channel of this lane
+  const bool has_c = c0 < D;
+  float M = kNegInf, wsum = 0.f, acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  constexpr int BATCH = 16;  // splits whose rows are in flight together
   for (int s0 = 0; s0 < ns; s0 += 64) {
     const int cnt = min(64, ns - s0);
-    const float w_l = lane < cnt ? fast_exp2((a.part_lse[base + s0 + lane] - Mb) * kLog2e) : 0.f;
-    const float* rows = a.part_o + (base + s0) * D;
+    const float lse_l = lane < cnt ? a.part_lse[base + s0 + lane] : kNegInf;
+    const float* rows = a.part_o + (base + s0) * D + c0;
+    float w_l = 0.f;
     for (int s1 = 0; s1 < cnt; s1 += BATCH) {
       float v[BATCH][PER];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const int c = lane + 64 * j;
-          v[u][j] = (s1 + u < cnt && c < D) ? rows[(size_t)(s1 + u) * D + c] : 0.f;
+      for (int u = 0; u < BATCH; ++u) {
+        const bool in = s1 + u < cnt && has_c;
+        const float* src = rows + (size_t)(in ? s1 + u : 0) * D;
+        if constexpr (PER == 4) {
+          const float4 x = in ? *reinterpret_cast<const float4*>(src) : float4{0.f, 0.f, 0.f, 0.f};
+          v[u][0] = x.x, v[u][1] = x.y, v[u][2] = x.z, v[u][3] = x.w;
+        } else if constexpr (PER == 2) {
+          const float2 x = in ? *reinterpret_cast<const float2*>(src) : float2{0.f, 0.f};
+          v[u][0] = x.x, v[u][1] = x.y;
+        } else {
+          v[u][0] = in ? src[0] : 0.f;
         }
+      }
+      if (s1 == 0) {
+        // this chunk's weights, while its first rows are in flight
+        float cm = lse_l;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cm = fmaxf(cm, xor_shfl(cm, off));
+        if (cm > M) {
+          const float alpha = M == kNegInf ? 0.f : fast_exp2((M - cm) * kLog2e);
+          wsum *= alpha;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) acc[j] *= alpha;
+          M = cm;
+        }
+        w_l = lane < cnt && M != kNegInf ? fast_exp2((lse_l - M) * kLog2e) : 0.f;
+        float ws = w_l;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ws += xor_shfl(ws, off);
+        wsum += ws;
+      }
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         // weight of split s0 + s1 + u (lanes at or past cnt hold 0)
-        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), (s1 + u) & 63));
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), (s1 + u) & 63));
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] = fmaf(ws, v[u][j], acc[j]);
+        for (int j = 0; j < PER; ++j) acc[j] = fmaf(wu, v[u][j], acc[j]);
       }
     }
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (has_c) {
+    const size_t i = ((size_t)b * a.H_q + h) * D + c0;
+    if (a.out_fp32) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int c = lane + 64 * j;
-    if (c < D) {
-      const size_t i = ((size_t)b * a.H_q + h) * D + c;
-      if (a.out_fp32)
-        static_cast<float*>(a.o)[i] = acc[j] * inv;
-      else
-        store_elem<T>(a.o, i, acc[j] * inv);
+      for (int j = 0; j < PER; ++j) static_cast<float*>(a.o)[i + j] = acc[j] * inv;
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) store_elem<T>(a.o, i + j, acc[j] * inv);
     }
   }
   if (a.lse != nullptr && lane == 0)
-    a.lse[(size_t)b * a.H_q + h] = wsum > 0.f ? Mb + __logf(wsum) : kNegInf;
+    a.lse[(size_t)b * a.H_q + h] = wsum > 0.f ? M + __logf(wsum) : kNegInf;
 }
 
 }  // namespace attn
