@@ -8,9 +8,10 @@
 // each K/V row is read ONCE for all G = H_q / H_kv query heads.
 //
 // Work split (persistent, balanced by bytes): the cache is cut into stages of
-// 16 tokens of one segment = (sequence, KV head [x group of 16 query heads]);
-// a stage is exactly one block of a paged cache ("KV Cache:推理慢的真正原因",
-// 工程优化手段 / 1. PagedAttention).  The stages of all segments, laid end to
+// one segment = (sequence, KV head [x group of 16 query heads]); a stage is
+// one block of 16 tokens of a paged cache ("KV Cache:推理慢的真正原因",
+// 工程优化手段 / 1. PagedAttention), or four blocks of a 4-bit cache, so that a
+// stage holds as many bytes.  The stages of all segments, laid end to
 // end, form one stream; the grid is a fixed number of waves (as many as fit
 // on the GPU at once) and wave k takes an equal contiguous share of the
 // stream.  A wave never waits for another:
@@ -20,7 +21,8 @@
 //    the non-temporal hint: they stream faster than global-to-LDS copies or
 //    ordinary loads on this part); the query
 //    rows of a segment are loaded with its first stage;
-//  * V goes through a 4 KB wave-private LDS tile to be read transposed;
+//  * V goes through a wave-private LDS tile (16-bit values, 16 rows per
+//    block) to be read transposed; 8- and 4-bit values are widened on the way;
 //  * S^T = K Q^T with v_mfma_f32_16x16x32 (16 tokens x 16 query heads, heads
 //    beyond G are don't-care columns), K rows read with ds_read_b128;
 //  * running (max, sum) per head; the reference maximum only moves when a
@@ -84,8 +86,13 @@ struct DecGeom {
   static constexpr int VCH = SLOT / 16 / 64;         // 16-byte chunks of V per lane per stage
   // V transposing read: a half-wave reads 8 consecutive rows at chunks {2m, 2m+1}.
   static __device__ __forceinline__ int swz_v(int r) { return 2 * ((r / RPL) % (CH / 2)); }
-  // Coalesced V stage copy: instruction i of lane l moves bytes 16 l + 1024 i of
-  // the stage, i.e. row crow(l) + i * 1024 / ROWB at chunk l % CH.
+  // V stage store: instruction i of lane l writes row crow(l) + i * 1024 / ROWB
+  // at chunk l % CH (16 lanes fill a 256-byte line in order).  Measured on this
+  // part with the LDS bank-conflict counter, this is conflict-free, while
+  // stores in which neighbouring lanes write chunks that are not neighbours
+  // (every second or fourth chunk of a row) are not, whatever the XOR.  So the
+  // 8- and 4-bit stages load 8 or 4 bytes per lane, which widen to exactly
+  // this one chunk.
   static __device__ __forceinline__ int crow(int l) { return l / CH; }
   static constexpr int CROW_STEP = 1024 / ROWB;
 };
@@ -108,6 +115,10 @@ __device__ __forceinline__ u32x4 load_stream(const uint8_t* p) {
 }
 __device__ __forceinline__ u32x2 load_stream8(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+template <typename VT>
+__device__ __forceinline__ VT load_stream_as(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const VT*>(p));
 }
 
 // Cache element formats of the decode kernel.
@@ -138,6 +149,11 @@ template <typename T>
 __device__ __forceinline__ void fp8x16_to(const u32x4 w, u32x4& lo, u32x4& hi) {
   lo = u32x4{fp8x2_to<T, false>(w[0]), fp8x2_to<T, true>(w[0]), fp8x2_to<T, false>(w[1]), fp8x2_to<T, true>(w[1])};
   hi = u32x4{fp8x2_to<T, false>(w[2]), fp8x2_to<T, true>(w[2]), fp8x2_to<T, false>(w[3]), fp8x2_to<T, true>(w[3])};
+}
+// 8 bytes of FP8 -> 8 values of T (one 16-byte vector)
+template <typename T>
+__device__ __forceinline__ u32x4 fp8x8_to(const u32x2 w) {
+  return u32x4{fp8x2_to<T, false>(w[0]), fp8x2_to<T, true>(w[0]), fp8x2_to<T, false>(w[1]), fp8x2_to<T, true>(w[1])};
 }
 
 // FP8 E4M3 codes -> the same values in T (exact), 16 per thread; used to hand
@@ -173,25 +189,50 @@ __device__ __forceinline__ uint32_t i8x2_to_f16(uint32_t xb) {
 // packed f16 add (- 1032) or FMA (* 1/16 - 72) per pair leaves the codes.  The
 // query fragments and the output rows follow the same slot order.
 __device__ __forceinline__ constexpr int kI4Slot(int e) { return ((e & 3) << 1) | (e >> 2); }
+// A RAW value v holds code c as 1024 + (c + 8) in slots 0, 1, 4, 5, so c =
+// v - kI4RawOff, and as 1024 + 16 (c + 8) in slots 2, 3, 6, 7, so c =
+// (v - kI4RawOff16) / 16.
+constexpr float kI4RawOff = 1032.f, kI4RawOff16 = 1152.f;
+// RAW keeps the biased values (1024 + u and 1024 + 16 u): the V path removes the
+// bias once from the normalised output, per slot (kI4RawOff, kI4RawOff16).
+template <bool RAW = false>
 __device__ __forceinline__ u32x4 i4x8_to_f16_slots(uint32_t w) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const uint32_t xb = w ^ 0x88888888u, x2 = xb >> 8;
-  const h2 t0 = __builtin_bit_cast(h2, (xb & 0x000F000Fu) | 0x64006400u);  // 1024 + u0, 1024 + u4
-  const h2 t1 = __builtin_bit_cast(h2, (xb & 0x00F000F0u) | 0x64006400u);  // 1024 + 16 u1, 1024 + 16 u5
-  const h2 t2 = __builtin_bit_cast(h2, (x2 & 0x000F000Fu) | 0x64006400u);  // 1024 + u2, 1024 + u6
-  const h2 t3 = __builtin_bit_cast(h2, (x2 & 0x00F000F0u) | 0x64006400u);  // 1024 + 16 u3, 1024 + 16 u7
+  const uint32_t r0 = (xb & 0x000F000Fu) | 0x64006400u;  // 1024 + u0, 1024 + u4
+  const uint32_t r1 = (xb & 0x00F000F0u) | 0x64006400u;  // 1024 + 16 u1, 1024 + 16 u5
+  const uint32_t r2 = (x2 & 0x000F000Fu) | 0x64006400u;  // 1024 + u2, 1024 + u6
+  const uint32_t r3 = (x2 & 0x00F000F0u) | 0x64006400u;  // 1024 + 16 u3, 1024 + 16 u7
+  if constexpr (RAW) return u32x4{r0, r1, r2, r3};
+  const h2 t0 = __builtin_bit_cast(h2, r0), t1 = __builtin_bit_cast(h2, r1);
+  const h2 t2 = __builtin_bit_cast(h2, r2), t3 = __builtin_bit_cast(h2, r3);
   const h2 off = h2{(_Float16)1032.f, (_Float16)1032.f};
   const h2 sixteenth = h2{(_Float16)0.0625f, (_Float16)0.0625f}, off16 = h2{(_Float16)-72.f, (_Float16)-72.f};
   return u32x4{__builtin_bit_cast(uint32_t, t0 - off), __builtin_bit_cast(uint32_t, t1 * sixteenth + off16),
                __builtin_bit_cast(uint32_t, t2 - off), __builtin_bit_cast(uint32_t, t3 * sixteenth + off16)};
 }
 
-// 16 int8 codes (words w[0..3]) -> 16 f16 values in two 16-byte vectors
-__device__ __forceinline__ void i8x16_to_f16(const u32x4 w, u32x4& lo, u32x4& hi) {
-  const u32x4 b = w ^ 0x80808080u;
-  lo = u32x4{i8x2_to_f16<false>(b[0]), i8x2_to_f16<true>(b[0]), i8x2_to_f16<false>(b[1]), i8x2_to_f16<true>(b[1])};
-  hi = u32x4{i8x2_to_f16<false>(b[2]), i8x2_to_f16<true>(b[2]), i8x2_to_f16<false>(b[3]), i8x2_to_f16<true>(b[3])};
+// 8 int8 codes (words w[0..1]) -> 8 f16 values.  After the XOR with 0x80 (byte
+// u = code + 128), one byte permute per pair builds the f16 words 0x64uu, i.e.
+// 1024 + u exactly (spacing 1 in [1024, 2048)); with SUB one packed f16 add of
+// -1152 per pair leaves the codes, without it the values keep the offset 1152
+// (the V path removes it once from the normalised output).
+template <bool SUB>
+__device__ __forceinline__ u32x4 i8x8_to_f16(const u32x2 w) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const u32x2 b = w ^ 0x80808080u;
+  // v_perm_b32 selectors: result bytes (low to high) = b0, 0x64, b1, 0x64 and b2, 0x64, b3, 0x64
+  auto pair = [](uint32_t x, uint32_t sel) {
+    const uint32_t r = __builtin_amdgcn_perm(0x64646464u, x, sel);
+    if constexpr (SUB)
+      return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, r) - h2{(_Float16)1152.f, (_Float16)1152.f});
+    else
+      return r;
+  };
+  constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;
+  return u32x4{pair(b[0], kLo), pair(b[0], kHi), pair(b[1], kLo), pair(b[1], kHi)};
 }
+constexpr float kI8Offset = 1152.f;  // V values before SUB: code + 1152
 
 // Int8 cache: the key scales fold into the query.  q'[c] = q[c] * s_k[g][c] in
 // fp32; each head's q' is multiplied by 2^(14 - e), with |q'| < 2^e for all its
@@ -251,9 +292,39 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   constexpr int ROWB = Gm::ROWB, VCH = Gm::VCH;
   // bytes per cache row, and 16-byte pieces of K and of V a lane loads per stage
   constexpr int RB = I4 ? D / 2 : (Q8 ? D : ROWB);
-  constexpr int NKL = I4 ? 1 : (Q8 ? D / 64 : KS), NVL = I4 ? 1 : (Q8 ? D / 64 : VCH);
+  constexpr int NKL = I4 ? 1 : (Q8 ? D / 64 : KS);
+  // V loads of an 8- or 4-bit cache.  Narrow (WV false): VCH loads per lane per
+  // block of VB bytes, each widening to one 16-byte chunk of the LDS tile, in
+  // the 16-bit stores' conflict-free order.  Wide (WV true): the 16-bit path's
+  // 16-byte loads (RB / 4 bytes at 4 bits), each widening to two (four) chunks
+  // of one row, stored with every second (fourth) chunk per instruction.
+  constexpr bool WV = Q8 && !I4;
+  constexpr int VB = !Q8 ? 16 : WV ? (I4 ? RB / 4 : 16) : (I4 ? 4 : 8);
+  constexpr int NV = !Q8 ? VCH : WV ? (I4 ? 1 : D / 64) : VCH;  // V loads per lane per block
+  using VT = typename std::conditional<VB == 16, u32x4,
+                                       typename std::conditional<VB == 8, u32x2, uint32_t>::type>::type;
+  // Physical 16-byte chunk of logical chunk c of tile row r.  The wide 8-bit
+  // stores write chunks 2m and 2m + 1 of a row from lane m, so neighbouring
+  // lanes write every second chunk; measured on this part, a 16-byte store is
+  // conflict-free when neighbouring lanes write neighbouring chunks, so these
+  // tiles rotate the chunk index (2m -> m, 2m + 1 -> m + CH / 2) before the
+  // per-line XOR, which keeps the transposing reads conflict-free as well.
+  constexpr bool ROT = Q8 && !I4 && WV;
+  auto vchunk = [](int r, int c) {
+    if constexpr (ROT)
+      return ((c >> 1) | ((c & 1) * (Gm::CH / 2))) ^ ((r / Gm::RPL) % (Gm::CH / 2));
+    else
+      return c ^ Gm::swz_v(r);
+  };
+  // Cache blocks per stage.  A 16-bit stage of one block is 128 bytes per lane
+  // at d = 128; an 8- or 4-bit stage takes as many blocks as give the same
+  // bytes, so the per-stage work (the softmax's reductions, the loop, the
+  // bookkeeping) is spread over as many bytes and as many bytes are in flight.
+  constexpr int SB = I4 ? 256 / RB : 1;
+  constexpr int TS = kDecStage * SB;  // tokens per stage
+  static_assert(!Q8 || PAGED, "8- and 4-bit caches are paged");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t vtile[kDecWaves * Gm::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t vtile[kDecWaves * Gm::SLOT * SB];
 
   const DecodeArgs& a = sa.a;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -274,7 +345,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     else if constexpr (Q8) return 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1);
     else return 32 * ks + 8 * grp;
   };
-  auto stages_of = [&](int len) { return (len + kDecStage - 1) / kDecStage; };
+  auto stages_of = [&](int len) { return (len + TS - 1) / TS; };
 
   // total stages (lanes read 64 lengths at a time) and this wave's share
   int total = 0;
@@ -351,7 +422,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const float c_log2 = a.scale_log2;  // > 0 on this path
   float cl = c_log2;                  // the segment's logit scale (int8: over the rescaled query)
-  uint8_t* vt = vtile + w * Gm::SLOT;
+  uint8_t* vt = vtile + w * Gm::SLOT * SB;
 
   // One stage in registers: K rows in MFMA operand layout (lane -> token row
   // col, 16 bytes at d = 32 ks + 8 grp), V rows as loaded (16-bit: bytes
@@ -359,85 +430,116 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // at byte RB / 4 (l % 4)), and the query fragments when the stage starts a
   // segment.
   struct Stage {
-    u32x4 k[NKL];
-    u32x4 v[NVL];
+    u32x4 k[SB][NKL];  // block j of the stage: tokens 16 j .. 16 j + 15
+    VT v[SB][NV];
     u32x4 q[KS];
     float qfac;  // int8: the query rows' scaling factor
-    bool ok;     // valid block id (paged)
+    bool ok;     // valid block ids (paged)
     bool qnew;   // q holds a new segment's query rows
   };
   // K and V loads come first and are unconditional (same count on every
   // path, so the compiler's vmcnt waits stay exact); query rows follow only
   // when the stage starts a segment.
-  // Paged: block id of the stage under cursor c, read one stage before its
-  // loads so the scalar load's latency hides behind the current stage.
-  auto block_of = [&](const Cursor& c) {
-    return PAGED ? table[(int64_t)c.b * a.max_blocks_per_seq + c.st] : 0;
+  // Paged: block ids of the stage under cursor c, read one stage before its
+  // loads so the scalar loads' latency hides behind the current stage.  A block
+  // of the stage that lies wholly past the sequence's length is not read from
+  // the table (its entry may be anything): block 0 of the stage stands in, and
+  // its rows get weight 0.
+  struct Blocks {
+    int id[SB];
   };
-  auto load = [&](const Cursor& c, const int blk, Stage& S) {
-    const int g = c.gh / sa.n_hg, hg = c.gh % sa.n_hg;
-    size_t row0;
-    S.ok = true;
-    if (PAGED) {
-      S.ok = blk >= 0 && blk < a.num_blocks;
-      row0 = ((size_t)(S.ok ? blk : 0) * a.H_kv + g) * kDecStage;
+  auto block_of = [&](const Cursor& c) {
+    Blocks r;
+    if constexpr (PAGED) {
+      const int32_t* row = table + (int64_t)c.b * a.max_blocks_per_seq + c.st * SB;
+      r.id[0] = row[0];
+#pragma unroll
+      for (int j = 1; j < SB; ++j) r.id[j] = (c.st * SB + j) * kDecStage < c.len ? row[j] : r.id[0];
     } else {
-      row0 = ((size_t)c.b * a.H_kv + g) * a.capacity + (size_t)c.st * kDecStage;
+      r.id[0] = 0;
     }
-    // contiguous: K rows past the capacity (last stage only) read the last row
-    // instead.  V rows past the sequence's length read its last row: their
-    // weights are 0, but a slot that was never written may hold a NaN or an
-    // infinity, and 0 times those is not 0 (K rows past the length are harmless:
-    // their scores are replaced by -inf).
-    const int kr = PAGED ? col : min(col, a.capacity - 1 - c.st * kDecStage);
-    const int vlim = c.len - 1 - c.st * kDecStage;  // >= 0: stage st starts inside the sequence
-    const int vr = min(l >> 2, vlim);
-    if constexpr (I4) {
-      // 4-bit rows: the 8-bit assignment at half the bytes (D / 8 bytes of K and
-      // of V per lane: one 16-byte load at d = 128, 8 bytes at d = 64)
-      const uint8_t* ks_src = kp + (row0 + kr) * RB + 4 * KS * grp;
-      const uint8_t* vs_src = vp + (row0 + vr) * RB + (RB / 4) * (l & 3);
-      if constexpr (D == 128) {
-        S.k[0] = load_stream(ks_src);
-        S.v[0] = load_stream(vs_src);
+    return r;
+  };
+  auto load = [&](const Cursor& c, const Blocks& blk, Stage& S) {
+    const int g = c.gh / sa.n_hg, hg = c.gh % sa.n_hg;
+    S.ok = true;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      // block j of the stage: tokens t1 .. t1 + 15 (block 0 again if it lies past the length)
+      const int t1 = c.st * TS + ((c.st * SB + j) * kDecStage < c.len ? j : 0) * kDecStage;
+      size_t row0;
+      if (PAGED) {
+        const bool ok = blk.id[j] >= 0 && blk.id[j] < a.num_blocks;
+        S.ok = S.ok && ok;
+        row0 = ((size_t)(ok ? blk.id[j] : 0) * a.H_kv + g) * kDecStage;
       } else {
-        const u32x2 k2 = load_stream8(ks_src), v2 = load_stream8(vs_src);
-        S.k[0] = u32x4{k2[0], k2[1], 0u, 0u};
-        S.v[0] = u32x4{v2[0], v2[1], 0u, 0u};
+        row0 = ((size_t)c.b * a.H_kv + g) * a.capacity + (size_t)t1;
       }
-    } else if (Q8) {
-      // 8-bit rows: load i of lane (col, grp) takes bytes 64 i + 16 grp of key
-      // row col, so one instruction covers 64 contiguous bytes of every row (as
-      // the 16-bit K loads do); the query fragments use the same assignment of
-      // d to k-steps (qd), so the dot products are unchanged.  V: the stage's
-      // rows are contiguous: instruction i of lane l moves their bytes
-      // 16 l + 1024 i (whole cache lines): row l / (RB / 16) + i 1024 / RB.
-      const uint8_t* ks_src = kp + (row0 + kr) * RB + 16 * grp;
+      // contiguous: K rows past the capacity (last stage only) read the last row
+      // instead.  V rows past the sequence's length read its last row: their
+      // weights are 0, but a slot that was never written may hold a NaN or an
+      // infinity, and 0 times those is not 0 (K rows past the length are harmless:
+      // their scores are replaced by -inf).
+      const int kr = PAGED ? col : min(col, a.capacity - 1 - t1);
+      const int vlim = c.len - 1 - t1;  // >= 0: the block starts inside the sequence
+      if constexpr (I4) {
+        // 4-bit rows: the 8-bit assignment at half the bytes (D / 8 bytes of K
+        // per lane: one 16-byte load at d = 128, 8 bytes at d = 64)
+        const uint8_t* ks_src = kp + (row0 + kr) * RB + 4 * KS * grp;
+        if constexpr (D == 128) {
+          S.k[j][0] = load_stream(ks_src);
+        } else {
+          const u32x2 k2 = load_stream8(ks_src);
+          S.k[j][0] = u32x4{k2[0], k2[1], 0u, 0u};
+        }
+      } else if constexpr (Q8) {
+        // 8-bit rows: load i of lane (col, grp) takes bytes 64 i + 16 grp of key
+        // row col, so one instruction covers 64 contiguous bytes of every row (as
+        // the 16-bit K loads do); the query fragments use the same assignment of
+        // d to k-steps (qd), so the dot products are unchanged.
+        const uint8_t* ks_src = kp + (row0 + kr) * RB + 16 * grp;
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) S.k[i] = load_stream(ks_src + 64 * i);
-      const int lim = min(kDecStage - 1, vlim);
+        for (int i = 0; i < NKL; ++i) S.k[j][i] = load_stream(ks_src + 64 * i);
+      } else {
+        // 16-bit rows: K goes straight into MFMA operand registers (each load
+        // instruction covers half of every row's 128-byte lines, the next one
+        // the other half).
+        const uint8_t* ks_src = kp + (row0 + kr) * ROWB + 16 * grp;
 #pragma unroll
-      for (int i = 0; i < NVL; ++i) {
-        const int r = min(l / (RB / 16) + i * (1024 / RB), lim);
-        S.v[i] = load_stream(vp + (row0 + r) * RB + 16 * (l % (RB / 16)));
+        for (int ks = 0; ks < KS; ++ks) S.k[j][ks] = load_stream(ks_src + 64 * ks);
       }
-    } else {
-      // 16-bit rows.  K goes straight into MFMA operand registers (each load
-      // instruction covers half of every row's 128-byte lines, the next one
-      // the other half).  The stage's V rows are contiguous: instruction i of
-      // lane l moves their bytes 16 l + 1024 i, so every V load covers whole
-      // cache lines; the transposing reads from LDS regroup them.  Contiguous
-      // cache: rows past the capacity read the last row instead; V rows past
-      // the sequence's length read its last row.
-      const int lim = min(kDecStage - 1, vlim);
-      const uint32_t cb = 16 * (l % Gm::CH);
-      const uint8_t* ks_src = kp + (row0 + kr) * ROWB + 16 * grp;
+      // V, every format: the block's rows are contiguous; instruction i of lane l
+      // reads VB bytes of row crow(l) + i CROW_STEP at VB (l % CH), so each
+      // instruction covers whole rows, and the bytes widen to the chunk the
+      // lane stores.  Paged: a block has all 16 rows, so the loads are one
+      // address plus constant offsets, and rows past the sequence's length are
+      // zeroed after the load (compute).  Contiguous: rows past the length
+      // read its last row instead (the last stage may end past the capacity).
+      if constexpr (Q8 && WV) {
+        // wide: 8-bit, instruction i of lane l reads 16 bytes of row l / (RB / 16) +
+        // i 1024 / RB at 16 (l % (RB / 16)); 4-bit, RB / 4 bytes of row l / 4 at
+        // RB / 4 (l % 4).  Rows past the length read its last row instead.
+        const int lim = min(kDecStage - 1, vlim);
+        if constexpr (I4) {
+          S.v[j][0] = load_stream_as<VT>(vp + (row0 + min(l >> 2, lim)) * RB + (RB / 4) * (l & 3));
+        } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) S.k[ks] = load_stream(ks_src + 64 * ks);
+          for (int i = 0; i < NV; ++i) {
+            const int r = min(l / (RB / 16) + i * (1024 / RB), lim);
+            S.v[j][i] = load_stream_as<VT>(vp + (row0 + r) * RB + 16 * (l % (RB / 16)));
+          }
+        }
+      } else if constexpr (PAGED) {
+        const uint8_t* vs_src = vp + (row0 + Gm::crow(l)) * RB + VB * (l % Gm::CH);
 #pragma unroll
-      for (int i = 0; i < VCH; ++i) {
-        const int r = min(Gm::crow(l) + i * Gm::CROW_STEP, lim);
-        S.v[i] = load_stream(vp + (row0 + r) * ROWB + cb);
+        for (int i = 0; i < VCH; ++i) S.v[j][i] = load_stream_as<VT>(vs_src + i * Gm::CROW_STEP * RB);
+      } else {
+        const int lim = min(kDecStage - 1, vlim);
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+          const int r = min(Gm::crow(l) + i * Gm::CROW_STEP, lim);
+          S.v[j][i] = load_stream_as<VT>(vp + (row0 + r) * RB + VB * (l % Gm::CH));
+        }
       }
     }
     S.qnew = seg_start(c);
@@ -471,13 +573,20 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     const int gi = 16 * hg + col;
     if (gi < G) {
       const size_t pidx = ((size_t)c.b * a.H_q + g * G + gi) * a.s_max + piece;
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const bool has_w = l_tot > 0.f;  // the piece has a key with weight > 0
+      const float inv = has_w ? 1.f / l_tot : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 o = oacc[db] * (FP8 ? inv * sa.v_scale : inv);
+        if constexpr (I8) o -= has_w ? kI8Offset : 0.f;  // V carried the codes + 1152
         if constexpr (I4) {
           // rows 16 db + 4 grp + i hold slots (4 grp + i) % 8 of their group of 8,
-          // i.e. channels c0 + {0, 4, 1, 5} with c0 = 16 db + 8 (grp / 2) + 2 (grp % 2)
+          // i.e. channels c0 + {0, 4, 1, 5} with c0 = 16 db + 8 (grp / 2) + 2 (grp % 2);
+          // i = 0, 1 are slots of the form 1024 + u, i = 2, 3 of the form 1024 + 16 u
+          if (has_w) {
+            o[0] -= kI4RawOff, o[1] -= kI4RawOff;
+            o[2] = (o[2] - kI4RawOff16) * 0.0625f, o[3] = (o[3] - kI4RawOff16) * 0.0625f;
+          }
           const int c0 = 16 * db + 8 * (grp >> 1) + 2 * (grp & 1);
           const float2 s01 = *reinterpret_cast<const float2*>(sa.v_scales + (size_t)g * D + c0);
           const float2 s45 = *reinterpret_cast<const float2*>(sa.v_scales + (size_t)g * D + c0 + 4);
@@ -519,61 +628,88 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       if (piece == 0 && l == 0)
         sa.piece_cnt[(size_t)c.b * a.H_q + c.gh] = (seg0 + c.n - 1) / share - seg0 / share + 1;
     }
-    // V rows into the LDS tile, and S^T = K Q^T: lane holds head col, tokens
-    // t0 + 4 grp + i.  An 8- or 4-bit stage is first widened to 16-bit values.
-    // put_v: the 4-bit layout (lane -> row l / 4, logical chunks VCH (l % 4) + i).
-    auto put_v = [&](const int i, const u32x4 x) {
-      const int r = l >> 2;
-      const int ch = (VCH * (l & 3) + i) ^ Gm::swz_v(r);
-      *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ch) = x;
-    };
-    const int t0 = c.st * kDecStage;
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (I4) {
+    // V rows into the LDS tile (widened to 16 bits: one chunk per load, at tile
+    // row 16 j + crow(l) + i CROW_STEP, chunk l % CH), and S^T = K Q^T per block
+    // j of the stage: lane holds head col, tokens t0 + 16 j + 4 grp + i.
+    const int t0 = c.st * TS;
+    f32x4 sacc[SB];
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) put_v(i, i4x8_to_f16_slots(S.v[0][i]));
+    for (int j = 0; j < SB; ++j) {
+      if constexpr (Q8 && WV) {
+        if constexpr (I4) {
+          // lane -> row l / 4, logical chunks VCH (l % 4) + i (word i of the load)
+          const int r = 16 * j + (l >> 2);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kw = i4x8_to_f16_slots(S.k[0][ks]);
-        sacc = mfma16k32<TC>(kw, qf[ks], sacc);
-        sacc = mfma16k32<TC>(kw, qlo[ks], sacc);
-      }
-    } else if constexpr (Q8) {
-      auto widen = [&](const u32x4 w, u32x4& lo, u32x4& hi) {
-        if constexpr (I8) i8x16_to_f16(w, lo, hi);
-        else fp8x16_to<T>(w, lo, hi);
-      };
-      // V: 16 values of row r at columns 16 (l % (RB / 16)), i.e. logical
-      // 16-bit chunks 2 (l % (RB / 16)) and the next one
+          for (int i = 0; i < D / 32; ++i) {
+            const int ch = vchunk(r, VCH * (l & 3) + i);
+            *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ch) = i4x8_to_f16_slots<true>(S.v[j][0][i]);
+          }
+        } else {
+          // 16 values of row r at columns 16 (l % (RB / 16)): logical chunks
+          // 2 (l % (RB / 16)) and the next one (int8: the codes + 1152)
 #pragma unroll
-      for (int i = 0; i < NVL; ++i) {
-        u32x4 lo, hi;
-        widen(S.v[i], lo, hi);
-        const int r = l / (RB / 16) + i * (1024 / RB), ch = 2 * (l % (RB / 16));
-        *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * (ch ^ Gm::swz_v(r))) = lo;
-        *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ((ch + 1) ^ Gm::swz_v(r))) = hi;
-      }
+          for (int i = 0; i < NV; ++i) {
+            const u32x2 w0 = u32x2{S.v[j][i][0], S.v[j][i][1]}, w1 = u32x2{S.v[j][i][2], S.v[j][i][3]};
+            const u32x4 lo = I8 ? i8x8_to_f16<false>(w0) : fp8x8_to<T>(w0);
+            const u32x4 hi = I8 ? i8x8_to_f16<false>(w1) : fp8x8_to<T>(w1);
+            const int r = 16 * j + l / (RB / 16) + i * (1024 / RB), ch = 2 * (l % (RB / 16));
+            *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = lo;
+            *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch + 1)) = hi;
+          }
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) {
-        u32x4 lo, hi;
-        widen(S.k[i], lo, hi);
-        sacc = mfma16k32<TC>(lo, qf[2 * i], sacc);
-        sacc = mfma16k32<TC>(hi, qf[2 * i + 1], sacc);
-        if constexpr (I8) {
-          sacc = mfma16k32<TC>(lo, qlo[2 * i], sacc);
-          sacc = mfma16k32<TC>(hi, qlo[2 * i + 1], sacc);
+        for (int i = 0; i < VCH; ++i) {
+          // paged: a row at or past the sequence's length (never written, perhaps
+          // NaN or infinite, and weighted 0) becomes 0 here, before the widening
+          VT raw = S.v[j][i];
+          if constexpr (PAGED) raw = t0 + 16 * j + Gm::crow(l) + i * Gm::CROW_STEP < c.len ? raw : VT{};
+          u32x4 x;
+          if constexpr (I4) {
+            x = i4x8_to_f16_slots<true>(raw);  // V: biased values, slot order
+          } else if constexpr (I8) {
+            x = i8x8_to_f16<false>(raw);      // V: the codes + 1152
+          } else if constexpr (FP8) {
+            x = fp8x8_to<T>(raw);
+          } else {
+            x = raw;
+          }
+          const int r = 16 * j + Gm::crow(l) + i * Gm::CROW_STEP, ch = l % Gm::CH;
+          *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = x;
         }
       }
-    } else {
-      // V rows into the LDS tile as loaded (row crow(l) + i CROW_STEP, logical
-      // chunk l % CH)
+      sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (I4) {
 #pragma unroll
-      for (int i = 0; i < VCH; ++i) {
-        const int r = Gm::crow(l) + i * Gm::CROW_STEP, ch = l % Gm::CH;
-        *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * (ch ^ Gm::swz_v(r))) = S.v[i];
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kw = i4x8_to_f16_slots(S.k[j][0][ks]);
+          sacc[j] = mfma16k32<TC>(kw, qf[ks], sacc[j]);
+          sacc[j] = mfma16k32<TC>(kw, qlo[ks], sacc[j]);
+        }
+      } else if constexpr (Q8) {
+        // K: 16 bytes per load, two k-steps (int8: exactly the codes)
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+          const u32x2 w0 = u32x2{S.k[j][i][0], S.k[j][i][1]}, w1 = u32x2{S.k[j][i][2], S.k[j][i][3]};
+          u32x4 lo, hi;
+          if constexpr (I8) {
+            lo = i8x8_to_f16<true>(w0);
+            hi = i8x8_to_f16<true>(w1);
+          } else {
+            lo = fp8x8_to<T>(w0);
+            hi = fp8x8_to<T>(w1);
+          }
+          sacc[j] = mfma16k32<TC>(lo, qf[2 * i], sacc[j]);
+          sacc[j] = mfma16k32<TC>(hi, qf[2 * i + 1], sacc[j]);
+          if constexpr (I8) {
+            sacc[j] = mfma16k32<TC>(lo, qlo[2 * i], sacc[j]);
+            sacc[j] = mfma16k32<TC>(hi, qlo[2 * i + 1], sacc[j]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sacc[j] = mfma16k32<T>(S.k[j][ks], qf[ks], sacc[j]);
       }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc = mfma16k32<T>(S.k[ks], qf[ks], sacc);
     }
     // Mask without a branch: the S^T accumulator is read right after the MFMA
     // that writes it, and the wait states that read needs are only inserted
@@ -581,9 +717,14 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     // read a stale accumulator register on one path (a segment's non-final
     // stages): the reference maximum of a column then came from stale data, and
     // at a segment start the O accumulator was not cleared for that column.
+    float tmax = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sacc[i] = (S.ok && t0 + 4 * grp + i < c.len) ? sacc[i] : kNegInf;
-    float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    for (int j = 0; j < SB; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc[j][i] = (S.ok && t0 + 16 * j + 4 * grp + i < c.len) ? sacc[j][i] : kNegInf;
+      tmax = fmaxf(tmax, fmaxf(fmaxf(sacc[j][0], sacc[j][1]), fmaxf(sacc[j][2], sacc[j][3])));
+    }
     tmax = fmaxf(tmax, xor_shfl(tmax, 16));
     tmax = max_pair32(tmax);
     const float mt = tmax * cl;
@@ -598,19 +739,26 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
     const float base = m == kNegInf ? 0.f : m;
-    float p[4];
+    u32x2 pf[SB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sacc[i], cl, -base));
-    const u32x2 pf = u32x2{cvt_pk<TC>(p[0], p[1]), cvt_pk<TC>(p[2], p[3])};
-    lsum = add_pair<TC>(pf[1], add_pair<TC>(pf[0], lsum));
-    lexact += (p[0] + p[1]) + (p[2] + p[3]);
+    for (int j = 0; j < SB; ++j) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sacc[j][i], cl, -base));
+      pf[j] = u32x2{cvt_pk<TC>(p[0], p[1]), cvt_pk<TC>(p[2], p[3])};
+      lsum = add_pair<TC>(pf[j][1], add_pair<TC>(pf[j][0], lsum));
+      lexact += (p[0] + p[1]) + (p[2] + p[3]);
+    }
     // O^T += V^T P^T (the wave's own LDS writes above precede these reads)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int ch = ((16 * db + 4 * vq) >> 3) ^ Gm::swz_v(vrow);
-      const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vt + vrow * ROWB + 16 * ch + 2 * ((4 * vq) & 7)));
-      oacc[db] = mfma16k16<TC>(vf, pf, oacc[db]);
+      const int ch = vchunk(vrow, (16 * db + 4 * vq) >> 3);
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vt + (16 * j + vrow) * ROWB + 16 * ch + 2 * ((4 * vq) & 7)));
+        oacc[db] = mfma16k16<TC>(vf, pf[j], oacc[db]);
+      }
     }
     if (c.st + 1 == c.n || last) finish(c);
   };
@@ -621,10 +769,10 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   Cursor cc = ic;
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // nblk: block id of stage ic (the dummy reloads past the end reuse it; load
-  // checks every id it is given)
+  // nblk: block ids of stage ic (the dummy reloads past the end reuse them;
+  // load checks every id it is given)
   Stage A, B;
-  int nblk = block_of(ic);
+  Blocks nblk = block_of(ic);
   load(ic, nblk, A);
   advance(ic);
   if (ic.pos < end) nblk = block_of(ic);

@@ -13,7 +13,8 @@ stale maximum for one query head now and then (a non-repeatable output).
 vector instruction that reads one of its result registers and counts the wait
 states.  For each MFMA opcode, the smallest count seen inside one basic block is
 taken as the compiler's own requirement; a path that crosses a block boundary with
-fewer is reported.  ``build.build()`` writes the assembly next to the library, and
+fewer is reported.  A path ends at an instruction that overwrites the result
+registers first (a load, or another vector instruction writing them).  ``build.build()`` writes the assembly next to the library, and
 tests/test_build_hazards.py runs this check on it.
 """
 from __future__ import annotations
@@ -23,6 +24,11 @@ import sys
 from typing import Dict, List, Tuple
 
 _ACCUMULATING = ("v_fmac", "v_dot2c", "v_mac", "v_fmamk", "v_fmaak")
+# instructions whose first operand is a vector register they write (loads and
+# vector ALU ops; comparisons and lane reads write scalar registers, which
+# _regs ignores)
+_WRITES_FIRST = ("v_", "global_load", "buffer_load", "flat_load", "scratch_load", "ds_read", "ds_bpermute",
+                 "ds_swizzle")
 
 
 def _regs(op: str) -> set:
@@ -103,22 +109,28 @@ def _reads(body: List[str], limit: int = 40):
             if not op.startswith("v_mfma") or not args:
                 continue
             dst = _regs(args[0])
-            stack, seen = [(b, i + 1, 0, False)], set()
+            stack, seen = [(b, i + 1, 0, False, frozenset(dst))], set()
             while stack:
                 state = stack.pop()
                 if state in seen:
                     continue
                 seen.add(state)
-                bb, j, w, crossed = state
+                bb, j, w, crossed, dst = state
                 ins, done = blocks[bb], False
+                live = set(dst)  # result registers not yet overwritten on this path
                 while j < len(ins):
                     op2, a2 = _split(ins[j])
                     if op2.startswith("v_") and not op2.startswith("v_mfma"):
                         srcs = set().union(*[_regs(a) for a in a2[1:]]) if len(a2) > 1 else set()
                         if op2.startswith(_ACCUMULATING) and a2:
                             srcs |= _regs(a2[0])
-                        if srcs & dst:
+                        if srcs & live:
                             found.append((op, w, crossed, bb, ins[j]))
+                            done = True
+                            break
+                    if a2 and op2.startswith(_WRITES_FIRST):
+                        live -= _regs(a2[0])  # a later write: the register no longer holds the result
+                        if not live:
                             done = True
                             break
                     w += int(a2[0], 0) + 1 if op2 == "s_nop" else 1
@@ -128,7 +140,7 @@ def _reads(body: List[str], limit: int = 40):
                     j += 1
                 if not done:
                     for sb in succ[bb]:
-                        stack.append((sb, 0, w, True))
+                        stack.append((sb, 0, w, True, frozenset(live)))
     return found
 
 
