@@ -278,8 +278,6 @@ def main() -> int:
     f8 = synth.fp8_prefill_inputs(pcase)
     q8, k8, v8 = (torch.from_numpy(f8[n]).cuda() for n in ("q", "k", "v"))
     del f8
-    f8_ws = torch.empty(K.attn_prefill_fp8_workspace_bytes(pcase.B, pcase.H_kv, pcase.N, pcase.d), dtype=torch.uint8,
-                        device="cuda")
     o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
     lse8 = torch.empty_like(lse)
 
@@ -387,7 +385,7 @@ def main() -> int:
         rec(11)
         K.attn_prefill_fp8(q8, k8, v8, causal=True, scale=pcase.sm_scale, q_scale=synth.FP8_Q_SCALE,
                            k_scale=synth.FP8_K_SCALE, v_scale=synth.FP8_V_SCALE,
-                           return_lse=True, workspace=f8_ws, out=o8, lse=lse8)
+                           return_lse=True, out=o8, lse=lse8)
         rec(12)
         K.kv_append_int4(i4_kp, i4_vp, g["k_new"], g["v_new"], g_lens, g_table, i4_ks, i4_vs)
         rec(13)
@@ -526,7 +524,7 @@ def main() -> int:
             **spread("fp8_prefill"),
             "speedup_vs_bf16": round(ms["prefill"] / ms["fp8_prefill"], 3),
             "roofline": roof("mfma", p8_tflops, round(PEAK_FP8_PREFILL_TFLOPS, 1), "TFLOP/s",
-                             "fp8_widen+prefill_mfma_kernel<BF16,128,causal,fp8>", {"flops": pf_flops}),
+                             "prefill_mfma_kernel<BF16,128,causal,fp8>", {"flops": pf_flops}),
         },
         "prefill_f16_small": {
             "value": round(s_tflops, 2), "unit": "TFLOP/s", "workload": scase.name + " (non-causal, no lse)",

@@ -256,18 +256,19 @@ int attn_decode_paged_int4(const void* q, const void* k_pool, const void* v_pool
  * o [B, H_q, N, d] in out_dtype (F16 or BF16), or fp32 when out_fp32 != 0 (the
  * same result before its rounding to out_dtype); lse as for attn_prefill.
  * Q K^T runs on the FP8 matrix cores (exact products, fp32 sums).  V's codes
- * are first widened (exactly) into `workspace` as out_dtype values, and P V
- * runs as in the 16-bit kernel, P rounded to out_dtype.
- * workspace: device, attn_prefill_fp8_workspace_bytes(B, H_kv, N, d) bytes.
+ * are widened (exactly) to out_dtype inside the kernel, on their way into
+ * on-chip memory, and P V runs as in the 16-bit kernel, P rounded to out_dtype.
+ * workspace, workspace_bytes: not used (no workspace is needed; NULL and 0 are
+ * fine), kept so that callers written for a workspace stay valid.
  * Errors: INVALID_ARG (pointers, sizes, scales, alignment), UNSUPPORTED
- *         (out_dtype, d not 64 / 128, scale <= 0), WORKSPACE, HIP.
+ *         (out_dtype, d not 64 / 128, scale <= 0), HIP.
  */
 int attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H_q, int H_kv, int N, int d, int causal, float scale,
                      float q_scale, float k_scale, float v_scale, int out_dtype,
                      int out_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of attn_prefill_fp8: 2 * B * H_kv * N * d (0 on invalid sizes). */
+/* Workspace bytes of attn_prefill_fp8: always 0 (V is widened inside the kernel). */
 size_t attn_prefill_fp8_workspace_bytes(int B, int H_kv, int N, int d);
 
 /*

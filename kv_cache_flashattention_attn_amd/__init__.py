@@ -475,8 +475,7 @@ def attn_prefill_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: 
     if out_dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("out_dtype must be torch.bfloat16 or torch.float16")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    nbytes = attn_prefill_fp8_workspace_bytes(B, H_kv, N, d)
-    workspace = _workspace(workspace, nbytes, q.device)
+    del workspace  # accepted for compatibility; the kernel widens V on chip and needs none
     out = _out(q, (B, H_q, N, d), out_fp32, out_dtype) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device)
@@ -484,7 +483,6 @@ def attn_prefill_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: 
                                 _dev(out, "out", torch.float32 if out_fp32 else out_dtype),
                                 _dev(lse, "lse", torch.float32) if return_lse else 0, B, H_q, H_kv, N, d,
                                 int(bool(causal)), scale, float(q_scale), float(k_scale), float(v_scale),
-                                DTYPE_CODES[out_dtype], int(bool(out_fp32)), _dev(workspace, "workspace"),
-                                workspace.numel() * workspace.element_size(), _stream())
+                                DTYPE_CODES[out_dtype], int(bool(out_fp32)), None, 0, _stream())
     _check("attn_prefill_fp8", rc)
     return (out, lse) if return_lse else out

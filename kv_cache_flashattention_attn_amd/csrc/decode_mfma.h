@@ -135,40 +135,6 @@ __device__ __forceinline__ int wave_sum(int x) {
 // nothing the kernel writes aliases them, so the compiler can read them with
 // scalar loads inside the stage loop (vector loads there would count against
 // the vmcnt waits of the stage copies).
-// Two FP8 E4M3 values (byte pair `hi` of word x) -> two 16-bit T values.  Every
-// E4M3 value is exact in bf16 and f16, so this is a pure format change.
-template <typename T, bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to(uint32_t x) {
-  if constexpr (std::is_same<T, BF16>::value)
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
-  else
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
-}
-// 16 bytes of FP8 (words w[0..3]) -> 16 values of T in two 16-byte vectors
-template <typename T>
-__device__ __forceinline__ void fp8x16_to(const u32x4 w, u32x4& lo, u32x4& hi) {
-  lo = u32x4{fp8x2_to<T, false>(w[0]), fp8x2_to<T, true>(w[0]), fp8x2_to<T, false>(w[1]), fp8x2_to<T, true>(w[1])};
-  hi = u32x4{fp8x2_to<T, false>(w[2]), fp8x2_to<T, true>(w[2]), fp8x2_to<T, false>(w[3]), fp8x2_to<T, true>(w[3])};
-}
-// 8 bytes of FP8 -> 8 values of T (one 16-byte vector)
-template <typename T>
-__device__ __forceinline__ u32x4 fp8x8_to(const u32x2 w) {
-  return u32x4{fp8x2_to<T, false>(w[0]), fp8x2_to<T, true>(w[0]), fp8x2_to<T, false>(w[1]), fp8x2_to<T, true>(w[1])};
-}
-
-// FP8 E4M3 codes -> the same values in T (exact), 16 per thread; used to hand
-// V to the 16-bit P V of the FP8 prefill.
-template <typename T>
-__global__ void __launch_bounds__(256) fp8_widen_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                        size_t n16) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n16) return;
-  u32x4 lo, hi;
-  fp8x16_to<T>(src[i], lo, hi);
-  dst[2 * i] = lo;
-  dst[2 * i + 1] = hi;
-}
-
 // Two int8 values (bytes 2 HI, 2 HI + 1 of x, already XORed with 0x80 so that
 // byte u = code + 128) -> two f16 values.  The f16 with bits 0x6400 | u is
 // 1024 + u exactly (spacing 1 in [1024, 2048)); subtracting 1152 leaves the code,

@@ -1,6 +1,7 @@
 // Helpers shared by the MFMA kernels of libattn (gfx950): 16-bit packing,
-// pair sums, lane exchanges and direct global -> LDS copies.
+// pair sums, lane exchanges, direct global -> LDS copies and FP8 widening.
 #pragma once
+#include <type_traits>
 #include "common.h"
 
 namespace attn {
@@ -97,6 +98,21 @@ __device__ __forceinline__ float sum_pair32(float x) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Two FP8 E4M3 values (byte pair `HI` of word x) -> two 16-bit T values.  Every
+// E4M3 value is exact in bf16 and f16, so this is a pure format change.
+template <typename T, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to(uint32_t x) {
+  if constexpr (std::is_same<T, BF16>::value)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
+}
+// 8 bytes of FP8 -> 8 values of T (one 16-byte vector)
+template <typename T>
+__device__ __forceinline__ u32x4 fp8x8_to(const u32x2 w) {
+  return u32x4{fp8x2_to<T, false>(w[0]), fp8x2_to<T, true>(w[0]), fp8x2_to<T, false>(w[1]), fp8x2_to<T, true>(w[1])};
 }
 
 }  // namespace attn

@@ -162,9 +162,11 @@ struct PagedKV {
 // from the table directly.
 constexpr int kLdsBlocks = 2048;
 
-// F8: Q and K are FP8 E4M3 codes (one byte per element) and Q K^T runs on the
-// FP8 matrix cores; V arrives as 16-bit values of T (the codes, widened
-// exactly by the caller) and P V runs in T as in the 16-bit kernel.
+// F8: Q, K and V are FP8 E4M3 codes (one byte per element) and Q K^T runs on
+// the FP8 matrix cores.  V tiles are read as codes into registers (8 bytes per
+// lane: the 8 channels of the chunk the 16-bit copy would move), widened
+// exactly to T and stored in the 16-bit tile layout, so P V runs in T as in the
+// 16-bit kernel; the codes never pass through memory widened.
 template <typename T, int D, int NW, bool CAUSAL, bool LSE, bool PAGED, bool F8 = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table,
@@ -370,6 +372,24 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
     }
   };
   auto issue_v = [&](int k0, int buf) { issue(vp, voff, 1, k0, buf); };
+  // F8 V: copy i of this lane = row r0 + i NW ROWS_PER_COPY of the tile, logical
+  // chunk l % CH (channels 8 (l % CH) .. + 7), as in the 16-bit copy
+  u32x2 v8[F8 ? Gm::COPIES : 1];
+  auto load_v8 = [&](int k0) {
+    const uint8_t* vb = static_cast<const uint8_t*>(a.v) + kv_base + 8 * (l % CH);
+#pragma unroll
+    for (int i = 0; i < Gm::COPIES; ++i) {
+      const int key = min(k0 + r0 + i * NW * Gm::ROWS_PER_COPY, a.N - 1);  // past the end: the last key
+      v8[i] = *reinterpret_cast<const u32x2*>(vb + (size_t)key * D);
+    }
+  };
+  auto store_v8 = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < Gm::COPIES; ++i) {
+      const int r = r0 + i * NW * Gm::ROWS_PER_COPY;
+      *reinterpret_cast<u32x4*>(&smem[buf][1][r * ROWB + 16 * ((l % CH) ^ Gm::swz_v(r))]) = fp8x8_to<T>(v8[i]);
+    }
+  };
   auto issue_v_full = [&](int k0, int buf) {  // a tile known to lie inside the sequence
     if (PAGED) {
       issue_paged(vp, vch, 1, k0, buf);
@@ -536,9 +556,13 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
     __syncthreads();
   }
   issue_k(0, 0);
-  issue_v(0, 0);
+  if constexpr (F8)
+    load_v8(0);
+  else
+    issue_v(0, 0);
   if (n_kt > 1) issue_k(BN, 1);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // own copies done
+  if constexpr (F8) store_v8(0);
   __syncthreads();
 
   f32x16 s_cur[2], s_nxt[2];
@@ -551,7 +575,10 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
   // the scheduler interleaves them; P V_j follows with its transposing reads.
   auto steady = [&](const int jj, f32x16* sc, f32x16* sn) {
     if (jj + 2 < n_kt) issue_k((jj + 2) * BN, jj & 1);
-    issue_v_full((jj + 1) * BN, (jj + 1) & 1);
+    if constexpr (F8)
+      load_v8((jj + 1) * BN);
+    else
+      issue_v_full((jj + 1) * BN, (jj + 1) & 1);
     row_max(jj, sc, false);
     qk(jj + 1, sn);
     softmax_pv(jj, sc);
@@ -568,6 +595,7 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA of P V
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // own copies of K_{j+2}, V_{j+1} done
+    if constexpr (F8) store_v8((jj + 1) & 1);
     __syncthreads();
   };
   for (; j + 2 < n_full; j += 2) {
@@ -585,12 +613,20 @@ prefill_mfma_kernel(PrefillArgs a, PagedKV pk, const int32_t* __restrict__ table
     const bool act = active(j);
     if (act) row_max(j, s_cur, j >= n_full);
     if (j + 2 < n_kt) issue_k((j + 2) * BN, j & 1);
-    if (j + 1 < n_kt) issue_v((j + 1) * BN, (j + 1) & 1);
+    if (j + 1 < n_kt) {
+      if constexpr (F8)
+        load_v8((j + 1) * BN);
+      else
+        issue_v((j + 1) * BN, (j + 1) & 1);
+    }
     if (j + 1 < n_kt && active(j + 1)) qk(j + 1, s_nxt);
     if (act) softmax_pv(j, s_cur);
     s_cur[0] = s_nxt[0];
     s_cur[1] = s_nxt[1];
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if constexpr (F8) {
+      if (j + 1 < n_kt) store_v8((j + 1) & 1);
+    }
     __syncthreads();
   }
   (void)CH;
