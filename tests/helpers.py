@@ -98,3 +98,14 @@ def assert_stored_output(o16, o32, ref: np.ndarray, dtype: str, what: str = "O")
         f"{what}: 16-bit output is not the round-to-nearest-even of the fp32 result"
     assert_close(values_of(o16), ref, dtype, what=what, storage_slack=True)
     return mx, mean
+
+
+def poison_table_tail(table, lens, num_blocks):
+    """The block table with every entry past each sequence's last block (the
+    sequence holds lens[b] keys) replaced by an id outside the pool: a kernel
+    that reads one of them raises the bad-block flag.  Numpy in, numpy out."""
+    t = table.copy()
+    for b in range(t.shape[0]):
+        used = -(-int(lens[b]) // 16)
+        t[b, used:] = -7 if b % 2 == 0 else num_blocks + 1000
+    return t

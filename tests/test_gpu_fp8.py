@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_lse_close, assert_stored_output, to_dev, to_dev_i32
+from helpers import poison_table_tail, assert_lse_close, assert_stored_output, to_dev, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -52,7 +52,7 @@ def test_fp8_append_image_is_bit_exact(K, dtype, scales):
     assert vp.cpu().numpy().tobytes() == cache.v.tobytes(), "V pool image differs"
 
 
-def run_fp8(K, case, lens=None, ks=synth.FP8_K_SCALE, vs=synth.FP8_V_SCALE, heads=None):
+def run_fp8(K, case, lens=None, ks=synth.FP8_K_SCALE, vs=synth.FP8_V_SCALE, heads=None, poison=False):
     """Append + decode over pools of every finite E4M3 code (empty slots hold NaN
     codes), checked with the stored-output rule: the fp32-output call meets the
     bar, the 16-bit output is its round-to-nearest-even."""
@@ -65,6 +65,8 @@ def run_fp8(K, case, lens=None, ks=synth.FP8_K_SCALE, vs=synth.FP8_V_SCALE, head
     q = to_dev(inp["q"], dt)
     K.kv_append_fp8(kp, vp, to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt), lens_d, table, ks, vs)
     seq = to_dev_i32(inp["lens"] + 1)
+    if poison:  # the decode must read no table entry past a sequence's last block
+        table = to_dev_i32(poison_table_tail(inp["block_table"], inp["lens"] + 1, kp.shape[0]))
     o, lse = K.attn_decode_paged_fp8(q, kp, vp, table, seq, k_scale=ks, v_scale=vs, scale=case.sm_scale,
                                      return_lse=True)
     o32 = K.attn_decode_paged_fp8(q, kp, vp, table, seq, k_scale=ks, v_scale=vs, scale=case.sm_scale,
@@ -116,3 +118,9 @@ def test_fp8_bad_block_raises_flag(K):
     K.attn_decode_paged_fp8(to_dev(inp["q"], "bf16"), u8(inp["k_pool"]), u8(inp["v_pool"]), to_dev_i32(table),
                             to_dev_i32(inp["lens"] + 1))
     assert K.attn_device_error_flags() & 2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_decode_reads_no_table_entry_past_the_length(K, d):
+    lens = np.array([0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 127, 128, 250], dtype=np.int32)
+    run_fp8(K, synth.DecodeCase("f8", len(lens), 8, 2, d, "bf16", 0, 260, True, 300 + d), lens=lens, poison=True)

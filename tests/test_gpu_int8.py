@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_lse_close, assert_stored_output, to_dev, to_dev_i32
+from helpers import poison_table_tail, assert_lse_close, assert_stored_output, to_dev, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -62,7 +62,7 @@ def test_int8_append_image_is_bit_exact(K, dtype, pow2):
     assert vp.cpu().numpy().tobytes() == cache.v.tobytes(), "V pool image differs"
 
 
-def run_int8(K, case, lens=None, heads=None):
+def run_int8(K, case, lens=None, heads=None, poison=False):
     print(f"[int8] {case}", flush=True)
     inp = synth.int8_decode_inputs(case, lens=lens)
     dt = case.dtype
@@ -73,6 +73,8 @@ def run_int8(K, case, lens=None, heads=None):
     q = to_dev(inp["q"], dt)
     K.kv_append_int8(kp, vp, to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt), lens_d, table, ks, vs)
     seq = to_dev_i32(inp["lens"] + 1)
+    if poison:  # the decode must read no table entry past a sequence's last block
+        table = to_dev_i32(poison_table_tail(inp["block_table"], inp["lens"] + 1, kp.shape[0]))
     o, lse = K.attn_decode_paged_int8(q, kp, vp, table, seq, ks, vs, scale=case.sm_scale, return_lse=True)
     o32 = K.attn_decode_paged_int8(q, kp, vp, table, seq, ks, vs, scale=case.sm_scale, out_fp32=True)
     torch.cuda.synchronize()
@@ -153,7 +155,7 @@ def u8(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).cuda()
 
 
-def run_int4(K, case, lens=None, heads=None):
+def run_int4(K, case, lens=None, heads=None, poison=False):
     print(f"[int4] {case}", flush=True)
     inp = synth.int4_decode_inputs(case, lens=lens)
     dt = case.dtype
@@ -164,6 +166,8 @@ def run_int4(K, case, lens=None, heads=None):
     q = to_dev(inp["q"], dt)
     K.kv_append_int4(kp, vp, to_dev(inp["k_new"], dt), to_dev(inp["v_new"], dt), lens_d, table, ks, vs)
     seq = to_dev_i32(inp["lens"] + 1)
+    if poison:  # the decode must read no table entry past a sequence's last block
+        table = to_dev_i32(poison_table_tail(inp["block_table"], inp["lens"] + 1, kp.shape[0]))
     o, lse = K.attn_decode_paged_int4(q, kp, vp, table, seq, ks, vs, scale=case.sm_scale, return_lse=True)
     o32 = K.attn_decode_paged_int4(q, kp, vp, table, seq, ks, vs, scale=case.sm_scale, out_fp32=True)
     torch.cuda.synchronize()
@@ -206,3 +210,22 @@ def test_int4_bad_block_raises_flag(K):
     K.attn_decode_paged_int4(to_dev(inp["q"], "bf16"), u8(inp["k_pool"]), u8(inp["v_pool"]), to_dev_i32(table),
                              to_dev_i32(inp["lens"] + 1), f32(inp["k_scales"]), f32(inp["v_scales"]))
     assert K.attn_device_error_flags() & 2
+
+
+# Lengths (after the append) around the 16-token blocks and the 64-token stages of
+# the 4-bit decode, with every table entry past a sequence's last block outside
+# the pool: a stage whose later blocks lie past the length must not read them.
+STAGE_TAIL_LENS = np.array([0, 1, 15, 16, 17, 31, 32, 33, 46, 47, 48, 62, 63, 64, 78, 126, 127, 128, 190, 250],
+                           dtype=np.int32)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_int4_decode_stage_tails_read_no_table_entry_past_the_length(K, d):
+    run_int4(K, synth.DecodeCase("i4", len(STAGE_TAIL_LENS), 8, 2, d, "bf16", 0, 260, True, 280 + d),
+             lens=STAGE_TAIL_LENS, poison=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_decode_reads_no_table_entry_past_the_length(K, d):
+    run_int8(K, synth.DecodeCase("i8", len(STAGE_TAIL_LENS), 8, 2, d, "f16", 0, 260, True, 290 + d),
+             lens=STAGE_TAIL_LENS, poison=True)
