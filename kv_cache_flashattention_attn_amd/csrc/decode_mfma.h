@@ -149,11 +149,12 @@ __device__ __forceinline__ uint32_t i8x2_to_f16(uint32_t xb) {
 }
 // 8 int4 codes (one word: byte b holds elements 2b (low nibble) and 2b + 1)
 // -> 8 f16 values in the order e0, e4, e1, e5, e2, e6, e3, e7 (element e in
-// 16-bit slot kI4Slot(e)).  With u = code + 8 (one XOR per word), each 16-bit
-// half of a word takes one nibble with one and-or: the f16 with bits 0x6400 | u
-// is 1024 + u and the one with 0x6400 | (u << 4) is 1024 + 16 u, exactly; one
-// packed f16 add (- 1032) or FMA (* 1/16 - 72) per pair leaves the codes.  The
-// query fragments and the output rows follow the same slot order.
+// 16-bit slot kI4Slot(e)).  With u = code + 8 (the nibble XOR 8), each 16-bit
+// half of a word takes one nibble with one three-input bit operation that also
+// applies the XOR: the f16 with bits 0x6400 | u is 1024 + u and the one with
+// 0x6400 | (u << 4) is 1024 + 16 u, exactly; one packed f16 add (- 1032) or FMA
+// (* 1/16 - 72) per pair leaves the codes.  The query fragments and the output
+// rows follow the same slot order.
 __device__ __forceinline__ constexpr int kI4Slot(int e) { return ((e & 3) << 1) | (e >> 2); }
 // A RAW value v holds code c as 1024 + (c + 8) in slots 0, 1, 4, 5, so c =
 // v - kI4RawOff, and as 1024 + 16 (c + 8) in slots 2, 3, 6, 7, so c =
@@ -164,11 +165,17 @@ constexpr float kI4RawOff = 1032.f, kI4RawOff16 = 1152.f;
 template <bool RAW = false>
 __device__ __forceinline__ u32x4 i4x8_to_f16_slots(uint32_t w) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const uint32_t xb = w ^ 0x88888888u, x2 = xb >> 8;
-  const uint32_t r0 = (xb & 0x000F000Fu) | 0x64006400u;  // 1024 + u0, 1024 + u4
-  const uint32_t r1 = (xb & 0x00F000F0u) | 0x64006400u;  // 1024 + 16 u1, 1024 + 16 u5
-  const uint32_t r2 = (x2 & 0x000F000Fu) | 0x64006400u;  // 1024 + u2, 1024 + u6
-  const uint32_t r3 = (x2 & 0x00F000F0u) | 0x64006400u;  // 1024 + 16 u3, 1024 + 16 u7
+  // ((w ^ 0x88888888) & mask) | 0x64006400 = (w & mask) ^ ((0x88888888 & mask) | 0x64006400),
+  // since the mask's bits and 0x64006400's are disjoint: one v_bitop3_b32 each
+  // (truth table 0x6A = (S0 & S1) ^ S2), the bias folded into the constant
+  auto pick = [](uint32_t x, uint32_t mask) {
+    return __builtin_amdgcn_bitop3_b32(x, mask, (0x88888888u & mask) | 0x64006400u, 0x6A);
+  };
+  const uint32_t x2 = w >> 8;
+  const uint32_t r0 = pick(w, 0x000F000Fu);   // 1024 + u0, 1024 + u4
+  const uint32_t r1 = pick(w, 0x00F000F0u);   // 1024 + 16 u1, 1024 + 16 u5
+  const uint32_t r2 = pick(x2, 0x000F000Fu);  // 1024 + u2, 1024 + u6
+  const uint32_t r3 = pick(x2, 0x00F000F0u);  // 1024 + 16 u3, 1024 + 16 u7
   if constexpr (RAW) return u32x4{r0, r1, r2, r3};
   const h2 t0 = __builtin_bit_cast(h2, r0), t1 = __builtin_bit_cast(h2, r1);
   const h2 t2 = __builtin_bit_cast(h2, r2), t3 = __builtin_bit_cast(h2, r3);
@@ -598,6 +605,23 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     // row 16 j + crow(l) + i CROW_STEP, chunk l % CH), and S^T = K Q^T per block
     // j of the stage: lane holds head col, tokens t0 + 16 j + 4 grp + i.
     const int t0 = c.st * TS;
+    // paged: rows at or past the sequence's length (never written, perhaps NaN
+    // or infinite, and weighted 0) become 0 before the widening; only the last
+    // stage of a segment has such rows, so the others skip the selects
+    VT vraw[SB][NV];
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) vraw[j][i] = S.v[j][i];
+    if constexpr (PAGED && !(Q8 && WV)) {
+      if (t0 + TS > c.len) {
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+#pragma unroll
+          for (int i = 0; i < VCH; ++i)
+            vraw[j][i] = t0 + 16 * j + Gm::crow(l) + i * Gm::CROW_STEP < c.len ? vraw[j][i] : VT{};
+      }
+    }
     f32x4 sacc[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
@@ -626,10 +650,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       } else {
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
-          // paged: a row at or past the sequence's length (never written, perhaps
-          // NaN or infinite, and weighted 0) becomes 0 here, before the widening
-          VT raw = S.v[j][i];
-          if constexpr (PAGED) raw = t0 + 16 * j + Gm::crow(l) + i * Gm::CROW_STEP < c.len ? raw : VT{};
+          const VT raw = vraw[j][i];
           u32x4 x;
           if constexpr (I4) {
             x = i4x8_to_f16_slots<true>(raw);  // V: biased values, slot order
