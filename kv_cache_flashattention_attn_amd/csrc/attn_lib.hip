@@ -72,7 +72,7 @@ int splits_for(int capacity) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t lse_off, cnt_off, q16_off, qfac_off, bytes;
+  size_t lse_off, cnt_off, qdig_off, qfac_off, bytes;
 };
 
 WorkspaceLayout workspace_layout(int B, int H_q, int capacity, int d) {
@@ -80,9 +80,10 @@ WorkspaceLayout workspace_layout(int B, int H_q, int capacity, int d) {
   WorkspaceLayout w;
   w.lse_off = align_up((size_t)B * H_q * S * d * sizeof(float), 256);
   w.cnt_off = align_up(w.lse_off + (size_t)B * H_q * S * sizeof(float), 256);
-  // int8 cache only: the scaled query as two f16 parts [B][H_q][2][d] and its factors [B][H_q]
-  w.q16_off = align_up(w.cnt_off + (size_t)B * H_q * sizeof(int32_t), 256);
-  w.qfac_off = align_up(w.q16_off + (size_t)B * H_q * 2 * d * sizeof(uint16_t), 256);
+  // int8 and int4 caches only: the scaled query as two int8 digits [B][H_q][2][d]
+  // and its factors [B][H_q]
+  w.qdig_off = align_up(w.cnt_off + (size_t)B * H_q * sizeof(int32_t), 256);
+  w.qfac_off = align_up(w.qdig_off + (size_t)B * H_q * 2 * d * sizeof(int8_t), 256);
   w.bytes = w.qfac_off + (size_t)B * H_q * sizeof(float);
   return w;
 }
@@ -212,8 +213,8 @@ struct CacheQuant {
   float k_scale = 1.f, v_scale = 1.f;              // FP8
   const float* k_scales = nullptr;                 // int8: [H_kv][d], device
   const float* v_scales = nullptr;
-  float* q_fac = nullptr;                          // int8: workspace [B][H_q]
-  uint16_t* q16 = nullptr;                         // int8: workspace [B][H_q][2][d] f16
+  float* q_fac = nullptr;                          // int8 / int4: workspace [B][H_q]
+  int8_t* qdig = nullptr;                          // int8 / int4: workspace [B][H_q][2][d] digits
 };
 
 template <typename T, int D, bool PAGED, int KV>
@@ -283,17 +284,17 @@ template <typename T, int KV>
 int decode_q8_typed(attn::DecodeArgs a, void* o, float* lse, int d, const CacheQuant& cq, int32_t* cnt,
                     hipStream_t st) {
   if (KV == attn::kKVInt8 || KV == attn::kKVInt4) {
-    // fold the key scales into an f16 copy of the query, which the decode reads instead
+    // fold the key scales into the query as two int8 digits, which the decode reads instead
     const int G = a.H_q / a.H_kv;
     if (d == 64)
       hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 64, KV == attn::kKVInt4>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
-                         cq.k_scales, cq.q16, cq.q_fac, a.H_q, G);
+                         cq.k_scales, cq.qdig, cq.q_fac, a.H_q, G);
     else
       hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 128, KV == attn::kKVInt4>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
-                         cq.k_scales, cq.q16, cq.q_fac, a.H_q, G);
+                         cq.k_scales, cq.qdig, cq.q_fac, a.H_q, G);
     const int rc = launch_status("attn_decode int8 query");
     if (rc != ATTN_OK) return rc;
-    a.q = cq.q16;
+    a.q = cq.qdig;
   }
   int rc = d == 64 ? launch_decode_mfma<T, 64, true, KV>(a, cnt, st, cq)
                    : launch_decode_mfma<T, 128, true, KV>(a, cnt, st, cq);
@@ -548,7 +549,7 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (q8) {
     CacheQuant cqw = cq;
-    cqw.q16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + lay.q16_off);
+    cqw.qdig = reinterpret_cast<int8_t*>(static_cast<char*>(workspace) + lay.qdig_off);
     cqw.q_fac = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.qfac_off);
     return dtype == ATTN_BF16 ? decode_q8_dispatch<attn::BF16>(a, o, lse, d, cqw, cnt, st)
                               : decode_q8_dispatch<attn::F16>(a, o, lse, d, cqw, cnt, st);

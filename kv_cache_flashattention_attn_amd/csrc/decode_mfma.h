@@ -23,8 +23,10 @@
 //    rows of a segment are loaded with its first stage;
 //  * V goes through a wave-private LDS tile (16-bit values, 16 rows per
 //    block) to be read transposed; 8- and 4-bit values are widened on the way;
-//  * S^T = K Q^T with v_mfma_f32_16x16x32 (16 tokens x 16 query heads, heads
-//    beyond G are don't-care columns), K rows read with ds_read_b128;
+//  * S^T = K Q^T (16 tokens x 16 query heads, heads beyond G are don't-care
+//    columns) with v_mfma_f32_16x16x32 on 16-bit and FP8 keys (FP8 widened in
+//    registers), or v_mfma_i32_16x16x64_i8 on int8 and int4 codes against the
+//    query's two int8 digits (decode_i8_query_kernel);
 //  * running (max, sum) per head; the reference maximum only moves when a
 //    stage exceeds it by 2^8, so the O accumulator is rarely rescaled;
 //  * O^T += V^T P^T with v_mfma_f32_16x16x16: P^T comes straight from the S^T
@@ -48,6 +50,14 @@ constexpr int kDecMinShare = 16;  // stages per wave at least (bounds the pieces
 // Pieces a segment of at most `capacity` tokens can be cut into.
 inline constexpr int dec_max_pieces(int capacity) {
   return (capacity + kDecStage * kDecMinShare - 1) / (kDecStage * kDecMinShare) + 1;
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// int8 x int8 -> int32, 16 x 16 output, 64-deep (gfx950): 16 bytes of A and of
+// B per lane; any assignment of the 64 k to lanes that A and B share gives the
+// same sums.
+__device__ __forceinline__ i32x4 mfma16k64_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
 }
 
 template <typename T>
@@ -103,7 +113,7 @@ struct DecodeStreamArgs {
   int n_hg;            // groups of 16 query heads per KV head
   float v_scale;       // fp8 cache: V = stored value * v_scale (1 otherwise)
   const float* v_scales;  // int8 cache: [H_kv][d] per-channel scales of V
-  const float* q_fac;     // int8 cache: [B][H_q] factor undoing the query's power-of-two scaling
+  const float* q_fac;     // int8 / int4 cache: [B][H_q] factor undoing the scaling of the query's digits
 };
 
 // Cache rows are read exactly once per step, so they are loaded with the
@@ -131,97 +141,70 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
-// lens and table repeat sa.a.seq_lens and sa.a.table as restrict parameters:
-// nothing the kernel writes aliases them, so the compiler can read them with
-// scalar loads inside the stage loop (vector loads there would count against
-// the vmcnt waits of the stage copies).
-// Two int8 values (bytes 2 HI, 2 HI + 1 of x, already XORed with 0x80 so that
-// byte u = code + 128) -> two f16 values.  The f16 with bits 0x6400 | u is
-// 1024 + u exactly (spacing 1 in [1024, 2048)); subtracting 1152 leaves the code,
-// exactly (one packed f16 add for the pair).
-template <bool HI>
-__device__ __forceinline__ uint32_t i8x2_to_f16(uint32_t xb) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const uint32_t y = HI ? (xb >> 16) : xb;
-  const uint32_t w = (y & 0xFFu) | ((y & 0xFF00u) << 8) | 0x64006400u;
-  const h2 r = __builtin_bit_cast(h2, w) - h2{(_Float16)1152.f, (_Float16)1152.f};
-  return __builtin_bit_cast(uint32_t, r);
-}
 // 8 int4 codes (one word: byte b holds elements 2b (low nibble) and 2b + 1)
-// -> 8 f16 values in the order e0, e4, e1, e5, e2, e6, e3, e7 (element e in
-// 16-bit slot kI4Slot(e)).  With u = code + 8 (the nibble XOR 8), each 16-bit
+// -> 8 biased f16 values in the order e0, e4, e1, e5, e2, e6, e3, e7 (element e
+// in 16-bit slot kI4Slot(e)).  With u = code + 8 (the nibble XOR 8), each 16-bit
 // half of a word takes one nibble with one three-input bit operation that also
 // applies the XOR: the f16 with bits 0x6400 | u is 1024 + u and the one with
-// 0x6400 | (u << 4) is 1024 + 16 u, exactly; one packed f16 add (- 1032) or FMA
-// (* 1/16 - 72) per pair leaves the codes.  The query fragments and the output
-// rows follow the same slot order.
+// 0x6400 | (u << 4) is 1024 + 16 u, exactly.  The V path keeps these biased
+// values and removes the bias once from the normalised output, per slot: a value
+// v holds code c as 1024 + (c + 8) in slots 0, 1, 4, 5, so c = v - kI4RawOff,
+// and as 1024 + 16 (c + 8) in slots 2, 3, 6, 7, so c = (v - kI4RawOff16) / 16.
+// The output rows are written back in channel order.
 __device__ __forceinline__ constexpr int kI4Slot(int e) { return ((e & 3) << 1) | (e >> 2); }
-// A RAW value v holds code c as 1024 + (c + 8) in slots 0, 1, 4, 5, so c =
-// v - kI4RawOff, and as 1024 + 16 (c + 8) in slots 2, 3, 6, 7, so c =
-// (v - kI4RawOff16) / 16.
 constexpr float kI4RawOff = 1032.f, kI4RawOff16 = 1152.f;
-// RAW keeps the biased values (1024 + u and 1024 + 16 u): the V path removes the
-// bias once from the normalised output, per slot (kI4RawOff, kI4RawOff16).
-template <bool RAW = false>
-__device__ __forceinline__ u32x4 i4x8_to_f16_slots(uint32_t w) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 i4x8_to_f16_biased(uint32_t w) {
   // ((w ^ 0x88888888) & mask) | 0x64006400 = (w & mask) ^ ((0x88888888 & mask) | 0x64006400),
   // since the mask's bits and 0x64006400's are disjoint: one v_bitop3_b32 each
   // (truth table 0x6A = (S0 & S1) ^ S2), the bias folded into the constant
-  auto pick = [](uint32_t x, uint32_t mask) {
+  auto pick = [](uint32_t x, uint32_t mask) -> uint32_t {
     return __builtin_amdgcn_bitop3_b32(x, mask, (0x88888888u & mask) | 0x64006400u, 0x6A);
   };
   const uint32_t x2 = w >> 8;
-  const uint32_t r0 = pick(w, 0x000F000Fu);   // 1024 + u0, 1024 + u4
-  const uint32_t r1 = pick(w, 0x00F000F0u);   // 1024 + 16 u1, 1024 + 16 u5
-  const uint32_t r2 = pick(x2, 0x000F000Fu);  // 1024 + u2, 1024 + u6
-  const uint32_t r3 = pick(x2, 0x00F000F0u);  // 1024 + 16 u3, 1024 + 16 u7
-  if constexpr (RAW) return u32x4{r0, r1, r2, r3};
-  const h2 t0 = __builtin_bit_cast(h2, r0), t1 = __builtin_bit_cast(h2, r1);
-  const h2 t2 = __builtin_bit_cast(h2, r2), t3 = __builtin_bit_cast(h2, r3);
-  const h2 off = h2{(_Float16)1032.f, (_Float16)1032.f};
-  const h2 sixteenth = h2{(_Float16)0.0625f, (_Float16)0.0625f}, off16 = h2{(_Float16)-72.f, (_Float16)-72.f};
-  return u32x4{__builtin_bit_cast(uint32_t, t0 - off), __builtin_bit_cast(uint32_t, t1 * sixteenth + off16),
-               __builtin_bit_cast(uint32_t, t2 - off), __builtin_bit_cast(uint32_t, t3 * sixteenth + off16)};
+  return u32x4{pick(w, 0x000F000Fu),    // 1024 + u0, 1024 + u4
+               pick(w, 0x00F000F0u),    // 1024 + 16 u1, 1024 + 16 u5
+               pick(x2, 0x000F000Fu),   // 1024 + u2, 1024 + u6
+               pick(x2, 0x00F000F0u)};  // 1024 + 16 u3, 1024 + 16 u7
 }
 
-// 8 int8 codes (words w[0..1]) -> 8 f16 values.  After the XOR with 0x80 (byte
-// u = code + 128), one byte permute per pair builds the f16 words 0x64uu, i.e.
-// 1024 + u exactly (spacing 1 in [1024, 2048)); with SUB one packed f16 add of
-// -1152 per pair leaves the codes, without it the values keep the offset 1152
-// (the V path removes it once from the normalised output).
-template <bool SUB>
-__device__ __forceinline__ u32x4 i8x8_to_f16(const u32x2 w) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+// 8 int8 codes (words w[0..1]) -> 8 biased f16 values.  After the XOR with 0x80
+// (byte u = code + 128), one byte permute per pair builds the f16 words 0x64uu,
+// i.e. 1024 + u exactly (spacing 1 in [1024, 2048)): the code + kI8Offset.  The
+// V path removes the offset once from the normalised output.
+__device__ __forceinline__ u32x4 i8x8_to_f16_biased(const u32x2 w) {
   const u32x2 b = w ^ 0x80808080u;
   // v_perm_b32 selectors: result bytes (low to high) = b0, 0x64, b1, 0x64 and b2, 0x64, b3, 0x64
-  auto pair = [](uint32_t x, uint32_t sel) {
-    const uint32_t r = __builtin_amdgcn_perm(0x64646464u, x, sel);
-    if constexpr (SUB)
-      return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, r) - h2{(_Float16)1152.f, (_Float16)1152.f});
-    else
-      return r;
-  };
+  auto pair = [](uint32_t x, uint32_t sel) { return __builtin_amdgcn_perm(0x64646464u, x, sel); };
   constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;
   return u32x4{pair(b[0], kLo), pair(b[0], kHi), pair(b[1], kLo), pair(b[1], kHi)};
 }
-constexpr float kI8Offset = 1152.f;  // V values before SUB: code + 1152
+constexpr float kI8Offset = 1152.f;  // widened int8 V values: code + 1152
 
-// Int8 cache: the key scales fold into the query.  q'[c] = q[c] * s_k[g][c] in
-// fp32; each head's q' is multiplied by 2^(14 - e), with |q'| < 2^e for all its
-// channels, so its largest element lies in [2^13, 2^14) (the logits stay far
-// from overflow), then split into two f16 parts, hi = f16(q') and lo =
-// f16(q' - hi): hi + lo carries about 22 bits, and each part times an integer
-// code is exact in the MFMA's fp32 products.  q16 holds [B][H_q][2][d] (hi row,
-// then lo row); q_fac = 2^(e - 14) undoes the factor in the logit scale.
-// I4SLOTS (int4 cache): within each aligned group of 8 channels, channel e is
-// stored in slot kI4Slot(e), the order in which i4x8_to_f16_slots widens keys.
-// One wave per (head, sequence).
-template <typename T, int D, bool I4SLOTS>
+// Integer caches: the key scales fold into the query, q'[c] = q[c] * s_k[g][c]
+// in fp32.  Each head's q' is scaled so that its largest element is 32512 and
+// rounded to an integer x, stored as two int8 digits, x = 256 hi + lo (hi in
+// [-127, 127], lo in [-128, 127]): Q K^T then runs on the int8 matrix cores,
+// exactly (int32 sums), against the key codes.  x carries 15 bits and a sign,
+// against 11 for a single f16.  q_fac undoes the scale in the logit scale:
+// max |q'| / 32512, and a further 1/16 for the int4 cache, whose codes enter the
+// products as bytes holding 16 times the code (kI4ByteOrder).  qdig holds
+// [B][H_q][2][d] bytes (hi row, then lo row); for the int4 cache, channel c is
+// stored at position kI4ByteOrder(c).  One wave per (head, sequence).
+//
+// kI4ByteOrder: a lane's 16 bytes of int4 keys (32 codes, channels c0 .. c0 + 31)
+// unpack to 32 bytes: word w (channels c0 + 8 w .. + 7) gives the even channels
+// of its 8 (low nibbles, shifted up) and then the odd ones (high nibbles), so
+// each 16 channels 16 k + j enter the int8 Q K^T in the order 0, 2, 4, 6, 1, 3,
+// 5, 7, 8, 10, 12, 14, 9, 11, 13, 15; the query's digits are stored likewise.
+__device__ __forceinline__ constexpr int kI4ByteOrder(int c) {
+  return (c & ~7) | ((c & 1) << 2) | ((c & 7) >> 1);
+}
+template <typename T, int D, bool I4>
 __global__ void __launch_bounds__(64)
-decode_i8_query_kernel(const void* __restrict__ q, const float* __restrict__ k_scales, uint16_t* __restrict__ q16,
+decode_i8_query_kernel(const void* __restrict__ q, const float* __restrict__ k_scales, int8_t* __restrict__ qdig,
                        float* __restrict__ q_fac, int H_q, int G) {
   constexpr int E = D / 64;
+  constexpr float kTop = 32512.f;  // 127 * 256: the largest |x|, so that hi stays in [-127, 127]
   const int h = blockIdx.x, b = blockIdx.y, l = threadIdx.x;
   const size_t row = ((size_t)b * H_q + h) * D;
   const float* sk = k_scales + (size_t)(h / G) * D;
@@ -234,31 +217,32 @@ decode_i8_query_kernel(const void* __restrict__ q, const float* __restrict__ k_s
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  // amax < 2^ex (ex from its exponent field), clamped so both powers are normal
-  int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126;
-  ex = ex < -100 ? -100 : (ex > 120 ? 120 : ex);
-  const float up = __uint_as_float((uint32_t)(127 + 14 - ex) << 23);
-  uint16_t* dst = q16 + 2 * row;
+  const float up = amax > 0.f ? kTop / amax : 0.f;
+  int8_t* dst = qdig + 2 * row;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float x = v[e] * up;
-    const uint16_t hi = f32_to_f16_bits(x);
+    const int x = (int)rintf(fminf(fmaxf(v[e] * up, -kTop), kTop));
+    const int hi = (x + 128) >> 8;  // floor((x + 128) / 256)
     const int c = l + 64 * e;
-    const int at = I4SLOTS ? ((c & ~7) | kI4Slot(c & 7)) : c;
-    dst[at] = hi;
-    dst[D + at] = f32_to_f16_bits(x - f16_bits_to_f32(hi));
+    const int at = I4 ? kI4ByteOrder(c) : c;
+    dst[at] = (int8_t)hi;
+    dst[D + at] = (int8_t)(x - 256 * hi);
   }
-  if (l == 0) q_fac[(size_t)b * H_q + h] = __uint_as_float((uint32_t)(127 - 14 + ex) << 23);
+  if (l == 0) q_fac[(size_t)b * H_q + h] = amax / kTop * (I4 ? 0.0625f : 1.f);
 }
 
+// lens and table repeat sa.a.seq_lens and sa.a.table as restrict parameters:
+// nothing the kernel writes aliases them, so the compiler can read them with
+// scalar loads inside the stage loop (vector loads there would count against
+// the vmcnt waits of the stage copies).
 template <typename T, int D, bool PAGED, int KV>
 __global__ void __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const int32_t* __restrict__ table) {
   using Gm = DecGeom<D>;
   constexpr bool FP8 = KV == kKVFp8, I8 = KV == kKVInt8, I4 = KV == kKVInt4, Q8 = KV != kKV16;
-  constexpr bool QS = I8 || I4;  // integer codes: key scales folded into an f16 query
-  // MFMA operand type: the query's type, except over an integer cache, where the
-  // codes, the scaled query and P are f16 (codes exact, 11-bit products)
+  constexpr bool QS = I8 || I4;  // integer codes: key scales folded into the query's int8 digits
+  // P V operand type: the query's type, except over an integer cache, where the
+  // widened V codes and P are f16 (codes exact, P to 11 bits)
   using TC = typename std::conditional<QS, F16, T>::type;
   constexpr int KS = D / 32;   // 32-deep k-steps of Q K^T
   constexpr int DB = D / 16;   // 16-wide blocks of d
@@ -309,13 +293,13 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   const int n_workers = gridDim.x * kDecWaves;
 
   auto clamp = [&](int n) { return n < 0 ? 0 : (n > a.capacity ? a.capacity : n); };
-  // d of the 8 values lane group grp contributes to k-step ks of Q K^T (K and
-  // the query fragments agree on it): 16-bit rows 32 ks + 8 grp; 8-bit rows
-  // 64 (ks / 2) + 16 grp + 8 (ks % 2) (each K load is 64 contiguous bytes of a
-  // row, widened into k-steps 2i and 2i + 1); 4-bit rows 8 KS grp + 8 ks.
+  // d of the 8 values lane group grp contributes to k-step ks of the 16-bit
+  // Q K^T (K and the query fragments agree on it): 16-bit rows 32 ks + 8 grp;
+  // FP8 rows 64 (ks / 2) + 16 grp + 8 (ks % 2) (each K load is 64 contiguous
+  // bytes of a row, widened into k-steps 2i and 2i + 1).  The int8 and int4
+  // caches take their query digits as bytes (the segment start below).
   auto qd = [&](int ks) {
-    if constexpr (I4) return 8 * KS * grp + 8 * ks;
-    else if constexpr (Q8) return 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1);
+    if constexpr (Q8) return 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1);
     else return 32 * ks + 8 * grp;
   };
   auto stages_of = [&](int len) { return (len + TS - 1) / TS; };
@@ -519,16 +503,30 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     if (S.qnew) {
       // query heads g*G + 16 hg + col (columns past the group repeat head g*G)
       const int gi = 16 * hg + col;
-      const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (QS ? 2 * D : D);
+      const size_t qhead = (size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0);
+      if constexpr (QS) {
+        // int8 digits of the scaled query (hi row, then lo row): k-step i of the
+        // int8 Q K^T takes the bytes the lane's keys give it: int8, bytes
+        // 64 i + 16 grp (as the K loads); int4, bytes D / 4 grp + 16 i (its keys'
+        // channels, in kI4ByteOrder)
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(qp) + qhead * 2 * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + qd(ks));
+        for (int i = 0; i < D / 64; ++i) {
+          const int at = I4 ? (D / 4) * grp + 16 * i : 64 * i + 16 * grp;
+          S.q[2 * i] = *reinterpret_cast<const u32x4*>(src + at);
+          S.q[2 * i + 1] = *reinterpret_cast<const u32x4*>(src + D + at);
+        }
+      } else {
+        const uint16_t* src = qp + qhead * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + qd(ks));
+      }
       if constexpr (QS) S.qfac = sa.q_fac[(size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)];
     }
   };
 
   // per-segment state
   u32x4 qf[KS];
-  u32x4 qlo[QS ? KS : 1];  // integer caches: the low f16 parts of the scaled query
   f32x4 oacc[DB];
   float m = kNegInf, lsum = 0.f, lexact = 0.f;
   int piece = 0;
@@ -580,16 +578,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       // New segment: clear the running state and O.
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = S.q[ks];
-      if constexpr (QS) {
-        cl = c_log2 * S.qfac;
-        // the low parts, loaded here (segment starts are rare): the wait also
-        // covers the next stage's loads, which were issued before this stage's compute
-        const int g = c.gh / sa.n_hg, gi = 16 * (c.gh % sa.n_hg) + col;
-        const uint16_t* src = qp + ((size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)) * (2 * D) + D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qlo[ks] = *reinterpret_cast<const u32x4*>(src + qd(ks));
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      }
+      if constexpr (QS) cl = c_log2 * S.qfac;
       m = kNegInf;
       lsum = 0.f;
       lexact = 0.f;
@@ -632,7 +621,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
 #pragma unroll
           for (int i = 0; i < D / 32; ++i) {
             const int ch = vchunk(r, VCH * (l & 3) + i);
-            *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ch) = i4x8_to_f16_slots<true>(S.v[j][0][i]);
+            *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ch) = i4x8_to_f16_biased(S.v[j][0][i]);
           }
         } else {
           // 16 values of row r at columns 16 (l % (RB / 16)): logical chunks
@@ -640,8 +629,8 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
 #pragma unroll
           for (int i = 0; i < NV; ++i) {
             const u32x2 w0 = u32x2{S.v[j][i][0], S.v[j][i][1]}, w1 = u32x2{S.v[j][i][2], S.v[j][i][3]};
-            const u32x4 lo = I8 ? i8x8_to_f16<false>(w0) : fp8x8_to<T>(w0);
-            const u32x4 hi = I8 ? i8x8_to_f16<false>(w1) : fp8x8_to<T>(w1);
+            const u32x4 lo = I8 ? i8x8_to_f16_biased(w0) : fp8x8_to<T>(w0);
+            const u32x4 hi = I8 ? i8x8_to_f16_biased(w1) : fp8x8_to<T>(w1);
             const int r = 16 * j + l / (RB / 16) + i * (1024 / RB), ch = 2 * (l % (RB / 16));
             *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = lo;
             *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch + 1)) = hi;
@@ -653,9 +642,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
           const VT raw = vraw[j][i];
           u32x4 x;
           if constexpr (I4) {
-            x = i4x8_to_f16_slots<true>(raw);  // V: biased values, slot order
+            x = i4x8_to_f16_biased(raw);  // V: biased values, slot order
           } else if constexpr (I8) {
-            x = i8x8_to_f16<false>(raw);      // V: the codes + 1152
+            x = i8x8_to_f16_biased(raw);      // V: the codes + 1152
           } else if constexpr (FP8) {
             x = fp8x8_to<T>(raw);
           } else {
@@ -666,32 +655,35 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
         }
       }
       sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (I4) {
+      if constexpr (QS) {
+        // the key codes against the query's two int8 digits on the int8 matrix
+        // cores: exact int32 sums, x = 256 hi + lo recombined exactly (each sum is
+        // below 2^22 in magnitude), then fp32.  int8: the codes as stored (16 bytes
+        // per k-step).  int4: each word of 8 codes unpacks to 8 bytes holding 16
+        // times the codes, even channels then odd (kI4ByteOrder), with one shift
+        // and two ANDs; the 1/16 is in the query's factor.
+        i32x4 ahi = i32x4{0, 0, 0, 0}, alo = i32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kw = i4x8_to_f16_slots(S.k[j][0][ks]);
-          sacc[j] = mfma16k32<TC>(kw, qf[ks], sacc[j]);
-          sacc[j] = mfma16k32<TC>(kw, qlo[ks], sacc[j]);
+        for (int i = 0; i < D / 64; ++i) {
+          u32x4 kb;
+          if constexpr (I4) {
+            const uint32_t w0 = S.k[j][0][2 * i], w1 = S.k[j][0][2 * i + 1];
+            kb = u32x4{(w0 << 4) & 0xF0F0F0F0u, w0 & 0xF0F0F0F0u, (w1 << 4) & 0xF0F0F0F0u, w1 & 0xF0F0F0F0u};
+          } else {
+            kb = S.k[j][i];
+          }
+          ahi = mfma16k64_i8(kb, qf[2 * i], ahi);
+          alo = mfma16k64_i8(kb, qf[2 * i + 1], alo);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[j][e] = (float)(ahi[e] * 256 + alo[e]);
       } else if constexpr (Q8) {
-        // K: 16 bytes per load, two k-steps (int8: exactly the codes)
+        // FP8 K: 16 bytes per load, widened into two k-steps
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
           const u32x2 w0 = u32x2{S.k[j][i][0], S.k[j][i][1]}, w1 = u32x2{S.k[j][i][2], S.k[j][i][3]};
-          u32x4 lo, hi;
-          if constexpr (I8) {
-            lo = i8x8_to_f16<true>(w0);
-            hi = i8x8_to_f16<true>(w1);
-          } else {
-            lo = fp8x8_to<T>(w0);
-            hi = fp8x8_to<T>(w1);
-          }
-          sacc[j] = mfma16k32<TC>(lo, qf[2 * i], sacc[j]);
-          sacc[j] = mfma16k32<TC>(hi, qf[2 * i + 1], sacc[j]);
-          if constexpr (I8) {
-            sacc[j] = mfma16k32<TC>(lo, qlo[2 * i], sacc[j]);
-            sacc[j] = mfma16k32<TC>(hi, qlo[2 * i + 1], sacc[j]);
-          }
+          sacc[j] = mfma16k32<TC>(fp8x8_to<T>(w0), qf[2 * i], sacc[j]);
+          sacc[j] = mfma16k32<TC>(fp8x8_to<T>(w1), qf[2 * i + 1], sacc[j]);
         }
       } else {
 #pragma unroll
