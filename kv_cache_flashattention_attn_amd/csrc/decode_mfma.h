@@ -250,14 +250,14 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // bytes per cache row, and 16-byte pieces of K and of V a lane loads per stage
   constexpr int RB = I4 ? D / 2 : (Q8 ? D : ROWB);
   constexpr int NKL = I4 ? 1 : (Q8 ? D / 64 : KS);
-  // V loads of an 8- or 4-bit cache.  Narrow (WV false): VCH loads per lane per
-  // block of VB bytes, each widening to one 16-byte chunk of the LDS tile, in
-  // the 16-bit stores' conflict-free order.  Wide (WV true): the 16-bit path's
-  // 16-byte loads (RB / 4 bytes at 4 bits), each widening to two (four) chunks
-  // of one row, stored with every second (fourth) chunk per instruction.
+  // V loads of an 8- or 4-bit cache.  Narrow (4-bit, WV false): VCH loads per
+  // lane per block of VB = 4 bytes, each widening to one 16-byte chunk of the
+  // LDS tile, in the 16-bit stores' conflict-free order.  Wide (8-bit, WV
+  // true): the 16-bit path's 16-byte loads, each widening to two chunks of one
+  // row, stored in the rotated chunk order (vchunk).
   constexpr bool WV = Q8 && !I4;
-  constexpr int VB = !Q8 ? 16 : WV ? (I4 ? RB / 4 : 16) : (I4 ? 4 : 8);
-  constexpr int NV = !Q8 ? VCH : WV ? (I4 ? 1 : D / 64) : VCH;  // V loads per lane per block
+  constexpr int VB = !Q8 ? 16 : WV ? 16 : 4;
+  constexpr int NV = WV ? D / 64 : VCH;  // V loads per lane per block
   using VT = typename std::conditional<VB == 16, u32x4,
                                        typename std::conditional<VB == 8, u32x2, uint32_t>::type>::type;
   // Physical 16-byte chunk of logical chunk c of tile row r.  The wide 8-bit
@@ -266,7 +266,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // conflict-free when neighbouring lanes write neighbouring chunks, so these
   // tiles rotate the chunk index (2m -> m, 2m + 1 -> m + CH / 2) before the
   // per-line XOR, which keeps the transposing reads conflict-free as well.
-  constexpr bool ROT = Q8 && !I4 && WV;
+  constexpr bool ROT = WV;
   auto vchunk = [](int r, int c) {
     if constexpr (ROT)
       return ((c >> 1) | ((c & 1) * (Gm::CH / 2))) ^ ((r / Gm::RPL) % (Gm::CH / 2));
@@ -472,19 +472,15 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       // address plus constant offsets, and rows past the sequence's length are
       // zeroed after the load (compute).  Contiguous: rows past the length
       // read its last row instead (the last stage may end past the capacity).
-      if constexpr (Q8 && WV) {
-        // wide: 8-bit, instruction i of lane l reads 16 bytes of row l / (RB / 16) +
-        // i 1024 / RB at 16 (l % (RB / 16)); 4-bit, RB / 4 bytes of row l / 4 at
-        // RB / 4 (l % 4).  Rows past the length read its last row instead.
+      if constexpr (WV) {
+        // wide 8-bit: instruction i of lane l reads 16 bytes of row l / (RB / 16) +
+        // i 1024 / RB at 16 (l % (RB / 16)).  Rows past the length read its last
+        // row instead.
         const int lim = min(kDecStage - 1, vlim);
-        if constexpr (I4) {
-          S.v[j][0] = load_stream_as<VT>(vp + (row0 + min(l >> 2, lim)) * RB + (RB / 4) * (l & 3));
-        } else {
 #pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            const int r = min(l / (RB / 16) + i * (1024 / RB), lim);
-            S.v[j][i] = load_stream_as<VT>(vp + (row0 + r) * RB + 16 * (l % (RB / 16)));
-          }
+        for (int i = 0; i < NV; ++i) {
+          const int r = min(l / (RB / 16) + i * (1024 / RB), lim);
+          S.v[j][i] = load_stream_as<VT>(vp + (row0 + r) * RB + 16 * (l % (RB / 16)));
         }
       } else if constexpr (PAGED) {
         const uint8_t* vs_src = vp + (row0 + Gm::crow(l)) * RB + VB * (l % Gm::CH);
@@ -602,7 +598,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     for (int j = 0; j < SB; ++j)
 #pragma unroll
       for (int i = 0; i < NV; ++i) vraw[j][i] = S.v[j][i];
-    if constexpr (PAGED && !(Q8 && WV)) {
+    if constexpr (PAGED && !WV) {
       if (t0 + TS > c.len) {
 #pragma unroll
         for (int j = 0; j < SB; ++j)
@@ -614,27 +610,17 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     f32x4 sacc[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      if constexpr (Q8 && WV) {
-        if constexpr (I4) {
-          // lane -> row l / 4, logical chunks VCH (l % 4) + i (word i of the load)
-          const int r = 16 * j + (l >> 2);
+      if constexpr (WV) {
+        // 8-bit V: 16 values of row r at columns 16 (l % (RB / 16)): logical
+        // chunks 2 (l % (RB / 16)) and the next one (int8: the codes + 1152)
 #pragma unroll
-          for (int i = 0; i < D / 32; ++i) {
-            const int ch = vchunk(r, VCH * (l & 3) + i);
-            *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * ch) = i4x8_to_f16_biased(S.v[j][0][i]);
-          }
-        } else {
-          // 16 values of row r at columns 16 (l % (RB / 16)): logical chunks
-          // 2 (l % (RB / 16)) and the next one (int8: the codes + 1152)
-#pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            const u32x2 w0 = u32x2{S.v[j][i][0], S.v[j][i][1]}, w1 = u32x2{S.v[j][i][2], S.v[j][i][3]};
-            const u32x4 lo = I8 ? i8x8_to_f16_biased(w0) : fp8x8_to<T>(w0);
-            const u32x4 hi = I8 ? i8x8_to_f16_biased(w1) : fp8x8_to<T>(w1);
-            const int r = 16 * j + l / (RB / 16) + i * (1024 / RB), ch = 2 * (l % (RB / 16));
-            *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = lo;
-            *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch + 1)) = hi;
-          }
+        for (int i = 0; i < NV; ++i) {
+          const u32x2 w0 = u32x2{S.v[j][i][0], S.v[j][i][1]}, w1 = u32x2{S.v[j][i][2], S.v[j][i][3]};
+          const u32x4 lo = I8 ? i8x8_to_f16_biased(w0) : fp8x8_to<T>(w0);
+          const u32x4 hi = I8 ? i8x8_to_f16_biased(w1) : fp8x8_to<T>(w1);
+          const int r = 16 * j + l / (RB / 16) + i * (1024 / RB), ch = 2 * (l % (RB / 16));
+          *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = lo;
+          *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch + 1)) = hi;
         }
       } else {
 #pragma unroll
@@ -690,20 +676,32 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
         for (int ks = 0; ks < KS; ++ks) sacc[j] = mfma16k32<T>(S.k[j][ks], qf[ks], sacc[j]);
       }
     }
-    // Mask without a branch: the S^T accumulator is read right after the MFMA
+    // 16-bit and FP8 keys: mask without a branch, as the S^T accumulator is read right after the MFMA
     // that writes it, and the wait states that read needs are only inserted
     // reliably within one basic block.  A branch here once let the row maximum
     // read a stale accumulator register on one path (a segment's non-final
     // stages): the reference maximum of a column then came from stale data, and
     // at a segment start the O accumulator was not cleared for that column.
+    // The int8 and int4 scores are converted from the integer sums by vector
+    // instructions, pinned here to the MFMAs' block (an empty asm statement
+    // that takes them, so the compiler cannot sink the conversions, which read
+    // the MFMA results, past the branch); the mask then sits behind a
+    // wave-uniform branch that skips it on every stage the sequence fills.
+    if constexpr (QS) {
+#pragma unroll
+      for (int j = 0; j < SB; ++j) asm volatile("" ::"v"(sacc[j][0]), "v"(sacc[j][1]), "v"(sacc[j][2]), "v"(sacc[j][3]));
+    }
+    if (!(QS && S.ok && t0 + TS <= c.len)) {
+      const int lim = S.ok ? c.len - t0 - 4 * grp : 0;  // rows 16 j + i below lim are keys
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[j][i] = 16 * j + i < lim ? sacc[j][i] : kNegInf;
+    }
     float tmax = kNegInf;
 #pragma unroll
-    for (int j = 0; j < SB; ++j) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sacc[j][i] = (S.ok && t0 + 16 * j + 4 * grp + i < c.len) ? sacc[j][i] : kNegInf;
+    for (int j = 0; j < SB; ++j)
       tmax = fmaxf(tmax, fmaxf(fmaxf(sacc[j][0], sacc[j][1]), fmaxf(sacc[j][2], sacc[j][3])));
-    }
     tmax = fmaxf(tmax, xor_shfl(tmax, 16));
     tmax = max_pair32(tmax);
     const float mt = tmax * cl;
@@ -728,16 +726,33 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       lsum = add_pair<TC>(pf[j][1], add_pair<TC>(pf[j][0], lsum));
       lexact += (p[0] + p[1]) + (p[2] + p[3]);
     }
-    // O^T += V^T P^T (the wave's own LDS writes above precede these reads)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    // O^T += V^T P^T (the wave's own LDS writes above precede these reads).
+    // Lane (i, g) of a transposing read holds V^T[16 db + i][4 g .. 4 g + 3] of
+    // block j, and pf[j] holds P^T[4 g .. 4 g + 3][head] of the same block, so
+    // with several blocks per stage two blocks pair into one 32-deep k-step
+    // (k = 8 g + e: e < 4 from block j, e >= 4 from block j + 1, the same order
+    // on both operands); the channel tiles go inside, so that consecutive MFMAs
+    // are independent.
+    auto vread = [&](int j, int db) {
       const int ch = vchunk(vrow, (16 * db + 4 * vq) >> 3);
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vt + (16 * j + vrow) * ROWB + 16 * ch + 2 * ((4 * vq) & 7)));
+    };
+    if constexpr (SB % 2 == 0) {
 #pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vt + (16 * j + vrow) * ROWB + 16 * ch + 2 * ((4 * vq) & 7)));
-        oacc[db] = mfma16k16<TC>(vf, pf[j], oacc[db]);
+      for (int j = 0; j < SB; j += 2) {
+        const u32x4 pp = u32x4{pf[j][0], pf[j][1], pf[j + 1][0], pf[j + 1][1]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 v0 = __builtin_bit_cast(u32x2, vread(j, db)), v1 = __builtin_bit_cast(u32x2, vread(j + 1, db));
+          oacc[db] = mfma16k32<TC>(u32x4{v0[0], v0[1], v1[0], v1[1]}, pp, oacc[db]);
+        }
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] = mfma16k16<TC>(vread(j, db), pf[j], oacc[db]);
     }
     if (c.st + 1 == c.n || last) finish(c);
   };
