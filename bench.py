@@ -507,7 +507,7 @@ def main() -> int:
             "append_ms": round(ms["int8_append"], 4),
             "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["int8_decode"], 3),
             "roofline": roof("hbm", i_gbs, PEAK_HBM_GBS, "GB/s",
-                             "decode_i8_query+decode_mfma_kernel<BF16,128,paged,int8>+merge", {"bytes": f_bytes}),
+                             "decode_mfma_kernel<BF16,128,paged,int8>+merge", {"bytes": f_bytes}),
         },
         "decode_paged_int4": {
             "value": round(i4_gbs, 1), "unit": "GB/s", "workload": fcase.name + " (int4 cache, per-channel scales)",
@@ -516,7 +516,7 @@ def main() -> int:
             "append_ms": round(ms["int4_append"], 4),
             "speedup_vs_bf16_cache": round(ms["paged_decode"] / ms["int4_decode"], 3),
             "roofline": roof("hbm", i4_gbs, PEAK_HBM_GBS, "GB/s",
-                             "decode_i8_query+decode_mfma_kernel<BF16,128,paged,int4>+merge", {"bytes": i4_bytes}),
+                             "decode_mfma_kernel<BF16,128,paged,int4>+merge", {"bytes": i4_bytes}),
         },
         "prefill_fp8": {
             "value": round(p8_tflops, 2), "unit": "TFLOP/s", "workload": pcase.name + " (FP8 E4M3 Q, K, V)",

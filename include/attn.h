@@ -335,11 +335,10 @@ int kv_append_int8(void* k_pool, void* v_pool, const void* k_new, const void* v_
                    const float* k_scales, const float* v_scales, void* stream);
 
 /* attn_decode_paged over the int8 pools: q, o [B, H_q, d] in `dtype` (F16 or
- * BF16), d = 64 or 128, scale > 0.  Same workspace as attn_decode_paged (its
- * last two regions hold the query with the key scales folded in).  The scores
- * are computed on the int8 matrix cores: the query times the key scales,
- * rescaled per head so that its largest element is 32512, is rounded to an
- * integer and stored as two int8 digits (16 bits with the sign), each
+ * BF16), d = 64 or 128, scale > 0.  Same workspace as attn_decode_paged.
+ * The scores are computed on the int8 matrix cores: the query times the key
+ * scales, rescaled per head so that its largest element is 32512, is rounded
+ * to an integer held as two int8 digits (16 bits with the sign), each
  * multiplied with the codes in exact int32 sums.
  * Errors: as attn_decode_paged; INVALID_ARG for null or misaligned scale arrays;
  *         UNSUPPORTED for other dtypes / d. */
@@ -374,12 +373,10 @@ int kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n_pairs
                    int block_size, int num_blocks, int elem_bytes, void* stream);
 
 /* Workspace bytes every decode call (attn_decode, attn_decode_paged and its
- * 8-bit forms) needs for a cache capacity of max_seq_len tokens per sequence.
- * Layout, each region 256-byte aligned: split partial outputs fp32
- * [B][H_q][S][d], their lse fp32 [B][H_q][S], piece counts int32 [B][H_q],
- * then (int8 and int4 caches only) the scaled query as two int8 digits
- * [B][H_q][2][d] and its factors fp32 [B][H_q]; S = ceil(max_seq_len / 256) + 1.  0 on invalid
- * sizes. */
+ * 8- and 4-bit forms) needs for a cache capacity of max_seq_len tokens per
+ * sequence.  Layout, each region 256-byte aligned: split partial outputs fp32
+ * [B][H_q][S][d], their lse fp32 [B][H_q][S], then piece counts int32
+ * [B][H_q]; S = ceil(max_seq_len / 256) + 1.  0 on invalid sizes. */
 size_t attn_decode_workspace_bytes(int B, int H_q, int max_seq_len, int d);
 
 /* Message describing the last error returned on the calling thread ("" if none). */

@@ -72,7 +72,7 @@ int splits_for(int capacity) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t lse_off, cnt_off, qdig_off, qfac_off, bytes;
+  size_t lse_off, cnt_off, bytes;
 };
 
 WorkspaceLayout workspace_layout(int B, int H_q, int capacity, int d) {
@@ -80,11 +80,7 @@ WorkspaceLayout workspace_layout(int B, int H_q, int capacity, int d) {
   WorkspaceLayout w;
   w.lse_off = align_up((size_t)B * H_q * S * d * sizeof(float), 256);
   w.cnt_off = align_up(w.lse_off + (size_t)B * H_q * S * sizeof(float), 256);
-  // int8 and int4 caches only: the scaled query as two int8 digits [B][H_q][2][d]
-  // and its factors [B][H_q]
-  w.qdig_off = align_up(w.cnt_off + (size_t)B * H_q * sizeof(int32_t), 256);
-  w.qfac_off = align_up(w.qdig_off + (size_t)B * H_q * 2 * d * sizeof(int8_t), 256);
-  w.bytes = w.qfac_off + (size_t)B * H_q * sizeof(float);
+  w.bytes = w.cnt_off + (size_t)B * H_q * sizeof(int32_t);
   return w;
 }
 
@@ -207,21 +203,19 @@ int launch_decode_plain(const attn::DecodeArgs& a, hipStream_t st) {
 }
 
 // How the cache stores K and V: 16-bit (the query's type), FP8 E4M3 with one
-// scale per tensor, or int8 with one scale per (KV head, channel).
+// scale per tensor, or int8 / int4 with one scale per (KV head, channel).
 struct CacheQuant {
   int kind = attn::kKV16;
   float k_scale = 1.f, v_scale = 1.f;              // FP8
-  const float* k_scales = nullptr;                 // int8: [H_kv][d], device
+  const float* k_scales = nullptr;                 // int8 / int4: [H_kv][d], device
   const float* v_scales = nullptr;
-  float* q_fac = nullptr;                          // int8 / int4: workspace [B][H_q]
-  int8_t* qdig = nullptr;                          // int8 / int4: workspace [B][H_q][2][d] digits
 };
 
 template <typename T, int D, bool PAGED, int KV>
 int launch_decode_mfma(const attn::DecodeArgs& a, int32_t* piece_cnt, hipStream_t st,
                        const CacheQuant& cq = CacheQuant()) {
   const int G = a.H_q / a.H_kv;
-  const attn::DecodeStreamArgs sa{a, piece_cnt, (G + 15) / 16, cq.v_scale, cq.v_scales, cq.q_fac};
+  const attn::DecodeStreamArgs sa{a, piece_cnt, (G + 15) / 16, cq.v_scale, cq.v_scales, cq.k_scales};
   const void* kernel = reinterpret_cast<const void*>(&attn::decode_mfma_kernel<T, D, PAGED, KV>);
   static int grid = 0;  // one value per instantiation; every device here is an MI355X
   if (grid == 0) grid = resident_grid(kernel, 64 * attn::kDecWaves);
@@ -279,23 +273,12 @@ int decode_dispatch(const attn::DecodeArgs& a, void* o, float* lse, int d, int d
   return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: dtype %d not supported", dtype);
 }
 
-// 8-bit paged cache (FP8 or int8): the MFMA decode widening K/V in registers, then the merge.
+// 8- and 4-bit paged cache (FP8, int8, int4): the MFMA decode (the integer
+// caches fold the key scales into the query's digits at each segment's start),
+// then the merge.
 template <typename T, int KV>
 int decode_q8_typed(attn::DecodeArgs a, void* o, float* lse, int d, const CacheQuant& cq, int32_t* cnt,
                     hipStream_t st) {
-  if (KV == attn::kKVInt8 || KV == attn::kKVInt4) {
-    // fold the key scales into the query as two int8 digits, which the decode reads instead
-    const int G = a.H_q / a.H_kv;
-    if (d == 64)
-      hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 64, KV == attn::kKVInt4>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
-                         cq.k_scales, cq.qdig, cq.q_fac, a.H_q, G);
-    else
-      hipLaunchKernelGGL((attn::decode_i8_query_kernel<T, 128, KV == attn::kKVInt4>), dim3(a.H_q, a.B), dim3(64), 0, st, a.q,
-                         cq.k_scales, cq.qdig, cq.q_fac, a.H_q, G);
-    const int rc = launch_status("attn_decode int8 query");
-    if (rc != ATTN_OK) return rc;
-    a.q = cq.qdig;
-  }
   int rc = d == 64 ? launch_decode_mfma<T, 64, true, KV>(a, cnt, st, cq)
                    : launch_decode_mfma<T, 128, true, KV>(a, cnt, st, cq);
   if (rc != ATTN_OK) return rc;
@@ -548,11 +531,8 @@ static int decode_common(const char* fn, bool paged, const void* q, const void* 
   int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.cnt_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (q8) {
-    CacheQuant cqw = cq;
-    cqw.qdig = reinterpret_cast<int8_t*>(static_cast<char*>(workspace) + lay.qdig_off);
-    cqw.q_fac = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.qfac_off);
-    return dtype == ATTN_BF16 ? decode_q8_dispatch<attn::BF16>(a, o, lse, d, cqw, cnt, st)
-                              : decode_q8_dispatch<attn::F16>(a, o, lse, d, cqw, cnt, st);
+    return dtype == ATTN_BF16 ? decode_q8_dispatch<attn::BF16>(a, o, lse, d, cq, cnt, st)
+                              : decode_q8_dispatch<attn::F16>(a, o, lse, d, cq, cnt, st);
   }
   return paged ? decode_dispatch<true>(a, o, lse, d, dtype, scale, cnt, st)
                : decode_dispatch<false>(a, o, lse, d, dtype, scale, cnt, st);

@@ -26,7 +26,7 @@
 //  * S^T = K Q^T (16 tokens x 16 query heads, heads beyond G are don't-care
 //    columns) with v_mfma_f32_16x16x32 on 16-bit and FP8 keys (FP8 widened in
 //    registers), or v_mfma_i32_16x16x64_i8 on int8 and int4 codes against the
-//    query's two int8 digits (decode_i8_query_kernel);
+//    query's two int8 digits (made at each segment's start, query_digits);
 //  * running (max, sum) per head; the reference maximum only moves when a
 //    stage exceeds it by 2^8, so the O accumulator is rarely rescaled;
 //  * O^T += V^T P^T with v_mfma_f32_16x16x16: P^T comes straight from the S^T
@@ -112,8 +112,8 @@ struct DecodeStreamArgs {
   int32_t* piece_cnt;  // [B][H_q]: pieces of segment (b, gh), written by the wave holding piece 0
   int n_hg;            // groups of 16 query heads per KV head
   float v_scale;       // fp8 cache: V = stored value * v_scale (1 otherwise)
-  const float* v_scales;  // int8 cache: [H_kv][d] per-channel scales of V
-  const float* q_fac;     // int8 / int4 cache: [B][H_q] factor undoing the scaling of the query's digits
+  const float* v_scales;  // int8 / int4 cache: [H_kv][d] per-channel scales of V
+  const float* k_scales;  // int8 / int4 cache: [H_kv][d] per-channel scales of K
 };
 
 // Cache rows are read exactly once per step, so they are loaded with the
@@ -180,56 +180,13 @@ __device__ __forceinline__ u32x4 i8x8_to_f16_biased(const u32x2 w) {
 }
 constexpr float kI8Offset = 1152.f;  // widened int8 V values: code + 1152
 
-// Integer caches: the key scales fold into the query, q'[c] = q[c] * s_k[g][c]
-// in fp32.  Each head's q' is scaled so that its largest element is 32512 and
-// rounded to an integer x, stored as two int8 digits, x = 256 hi + lo (hi in
-// [-127, 127], lo in [-128, 127]): Q K^T then runs on the int8 matrix cores,
-// exactly (int32 sums), against the key codes.  x carries 15 bits and a sign,
-// against 11 for a single f16.  q_fac undoes the scale in the logit scale:
-// max |q'| / 32512, and a further 1/16 for the int4 cache, whose codes enter the
-// products as bytes holding 16 times the code (kI4ByteOrder).  qdig holds
-// [B][H_q][2][d] bytes (hi row, then lo row); for the int4 cache, channel c is
-// stored at position kI4ByteOrder(c).  One wave per (head, sequence).
-//
-// kI4ByteOrder: a lane's 16 bytes of int4 keys (32 codes, channels c0 .. c0 + 31)
+// kI4Channel: a lane's 16 bytes of int4 keys (32 codes, channels c0 .. c0 + 31)
 // unpack to 32 bytes: word w (channels c0 + 8 w .. + 7) gives the even channels
 // of its 8 (low nibbles, shifted up) and then the odd ones (high nibbles), so
-// each 16 channels 16 k + j enter the int8 Q K^T in the order 0, 2, 4, 6, 1, 3,
-// 5, 7, 8, 10, 12, 14, 9, 11, 13, 15; the query's digits are stored likewise.
-__device__ __forceinline__ constexpr int kI4ByteOrder(int c) {
-  return (c & ~7) | ((c & 1) << 2) | ((c & 7) >> 1);
-}
-template <typename T, int D, bool I4>
-__global__ void __launch_bounds__(64)
-decode_i8_query_kernel(const void* __restrict__ q, const float* __restrict__ k_scales, int8_t* __restrict__ qdig,
-                       float* __restrict__ q_fac, int H_q, int G) {
-  constexpr int E = D / 64;
-  constexpr float kTop = 32512.f;  // 127 * 256: the largest |x|, so that hi stays in [-127, 127]
-  const int h = blockIdx.x, b = blockIdx.y, l = threadIdx.x;
-  const size_t row = ((size_t)b * H_q + h) * D;
-  const float* sk = k_scales + (size_t)(h / G) * D;
-  float v[E];
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    v[e] = load_elem<T>(q, row + l + 64 * e) * sk[l + 64 * e];
-    amax = fmaxf(amax, fabsf(v[e]));
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  const float up = amax > 0.f ? kTop / amax : 0.f;
-  int8_t* dst = qdig + 2 * row;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int x = (int)rintf(fminf(fmaxf(v[e] * up, -kTop), kTop));
-    const int hi = (x + 128) >> 8;  // floor((x + 128) / 256)
-    const int c = l + 64 * e;
-    const int at = I4 ? kI4ByteOrder(c) : c;
-    dst[at] = (int8_t)hi;
-    dst[D + at] = (int8_t)(x - 256 * hi);
-  }
-  if (l == 0) q_fac[(size_t)b * H_q + h] = amax / kTop * (I4 ? 0.0625f : 1.f);
-}
+// byte p of each 16 enters the int8 Q K^T with channel kI4Channel(p) of its 16:
+// 0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15.  The query's digits are
+// placed likewise.
+__device__ __forceinline__ constexpr int kI4Channel(int p) { return (p & 8) | ((p & 3) << 1) | ((p >> 2) & 1); }
 
 // lens and table repeat sa.a.seq_lens and sa.a.table as restrict parameters:
 // nothing the kernel writes aliases them, so the compiler can read them with
@@ -279,9 +236,15 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // bookkeeping) is spread over as many bytes and as many bytes are in flight.
   constexpr int SB = I4 ? 256 / RB : 1;
   constexpr int TS = kDecStage * SB;  // tokens per stage
+  // vector memory instructions every stage's load issues (K, then V), before
+  // any query row or key-scale copy
+  constexpr int kStageLoads = SB * (NKL + NV);
   static_assert(!Q8 || PAGED, "8- and 4-bit caches are paged");
 
   __shared__ __attribute__((aligned(1024))) uint8_t vtile[kDecWaves * Gm::SLOT * SB];
+  // int8 / int4: two slots per wave for the key scales of a segment's KV head,
+  // copied from global memory with the stage that starts the segment
+  __shared__ __attribute__((aligned(16))) float sktile[QS ? kDecWaves * 2 * D : 1];
 
   const DecodeArgs& a = sa.a;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -302,6 +265,26 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     if constexpr (Q8) return 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1);
     else return 32 * ks + 8 * grp;
   };
+  // int8 / int4: first of the 16 channels whose query digits k-step i of the
+  // int8 Q K^T takes from lane group grp: the channels its keys give it (int8,
+  // bytes 64 i + 16 grp of a row, as the K loads; int4, the 32 codes D / 4 grp
+  // .. + 31 unpacked, k-step i taking 16 of them in kI4Channel order)
+  auto qs_base = [&](int i) { return I4 ? (D / 4) * grp + 16 * i : 64 * i + 16 * grp; };
+  int skslot = 0;  // next LDS slot for a segment's key scales
+  // Paged loads, per-lane byte offsets from a block's first row.  K: 16-bit
+  // rows, lane (col, grp) takes bytes 16 grp (+ 64 ks) of row col, so each
+  // instruction covers half of every row's 128-byte lines and the next one the
+  // other half, straight into MFMA operand layout; 8-bit rows, bytes 16 grp (+
+  // 64 i) of row col, so one instruction covers 64 contiguous bytes of every
+  // row (the query fragments use the same assignment of d to k-steps, qd);
+  // 4-bit rows, D / 8 bytes at D / 8 grp (one 16-byte load at d = 128, 8 bytes
+  // at d = 64).  V (16-bit and 4-bit): VB bytes of row crow(l) + i CROW_STEP at
+  // VB (l % CH), so each instruction covers whole rows and the bytes widen to
+  // the chunk the lane stores; the wide 8-bit loads take 16 bytes of row
+  // l / (RB / 16) + i 1024 / RB at 16 (l % (RB / 16)) (in load).
+  const uint32_t klane = I4 ? col * RB + (D / 8) * grp : col * RB + 16 * grp;
+  const uint32_t vlane = Gm::crow(l) * RB + VB * (l % Gm::CH);
+  constexpr int VSTEP = Gm::CROW_STEP * RB;
   auto stages_of = [&](int len) { return (len + TS - 1) / TS; };
 
   // total stages (lanes read 64 lengths at a time) and this wave's share
@@ -390,9 +373,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     u32x4 k[SB][NKL];  // block j of the stage: tokens 16 j .. 16 j + 15
     VT v[SB][NV];
     u32x4 q[KS];
-    float qfac;  // int8: the query rows' scaling factor
     bool ok;     // valid block ids (paged)
     bool qnew;   // q holds a new segment's query rows
+    int skslot;  // int8 / int4, qnew: LDS slot holding the segment's key scales
   };
   // K and V loads come first and are unconditional (same count on every
   // path, so the compiler's vmcnt waits stay exact); query rows follow only
@@ -432,66 +415,50 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       } else {
         row0 = ((size_t)c.b * a.H_kv + g) * a.capacity + (size_t)t1;
       }
-      // contiguous: K rows past the capacity (last stage only) read the last row
+      // K and V of block j: the block's rows start at byte row0 * RB of the
+      // pool (the same offset in both pools), a wave-uniform base; each lane
+      // adds a constant offset (klane, vlane) and each instruction an immediate,
+      // so the loads need no per-lane address arithmetic.
+      // Contiguous: K rows past the capacity (last stage only) read the last row
       // instead.  V rows past the sequence's length read its last row: their
       // weights are 0, but a slot that was never written may hold a NaN or an
       // infinity, and 0 times those is not 0 (K rows past the length are harmless:
-      // their scores are replaced by -inf).
-      const int kr = PAGED ? col : min(col, a.capacity - 1 - t1);
-      const int vlim = c.len - 1 - t1;  // >= 0: the block starts inside the sequence
-      if constexpr (I4) {
-        // 4-bit rows: the 8-bit assignment at half the bytes (D / 8 bytes of K
-        // per lane: one 16-byte load at d = 128, 8 bytes at d = 64)
-        const uint8_t* ks_src = kp + (row0 + kr) * RB + 4 * KS * grp;
-        if constexpr (D == 128) {
-          S.k[j][0] = load_stream(ks_src);
-        } else {
-          const u32x2 k2 = load_stream8(ks_src);
+      // their scores are replaced by -inf).  Paged: a block has all 16 rows; the
+      // wide 8-bit V loads clamp their row likewise (measured faster here than
+      // zeroing), the others read every row and zero those past the length
+      // after the load (compute).
+      const uint8_t* kb = kp + row0 * RB;
+      const uint8_t* vb = vp + row0 * RB;
+      if constexpr (PAGED) {
+        if constexpr (I4 && D == 64) {
+          const u32x2 k2 = load_stream8(kb + klane);
           S.k[j][0] = u32x4{k2[0], k2[1], 0u, 0u};
-        }
-      } else if constexpr (Q8) {
-        // 8-bit rows: load i of lane (col, grp) takes bytes 64 i + 16 grp of key
-        // row col, so one instruction covers 64 contiguous bytes of every row (as
-        // the 16-bit K loads do); the query fragments use the same assignment of
-        // d to k-steps (qd), so the dot products are unchanged.
-        const uint8_t* ks_src = kp + (row0 + kr) * RB + 16 * grp;
+        } else {
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) S.k[j][i] = load_stream(ks_src + 64 * i);
+          for (int i = 0; i < NKL; ++i) S.k[j][i] = load_stream(kb + klane + 64 * i);
+        }
+        if constexpr (WV) {
+          const int lim = min(kDecStage - 1, c.len - 1 - t1);
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const int r = min(l / (RB / 16) + i * (1024 / RB), lim);
+            S.v[j][i] = load_stream_as<VT>(vb + r * RB + 16 * (l % (RB / 16)));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < NV; ++i) S.v[j][i] = load_stream_as<VT>(vb + vlane + i * VSTEP);
+        }
       } else {
-        // 16-bit rows: K goes straight into MFMA operand registers (each load
-        // instruction covers half of every row's 128-byte lines, the next one
-        // the other half).
-        const uint8_t* ks_src = kp + (row0 + kr) * ROWB + 16 * grp;
+        const int kr = min(col, a.capacity - 1 - t1);
+        const int vlim = c.len - 1 - t1;  // >= 0: the block starts inside the sequence
+        const uint8_t* ks_src = kb + kr * ROWB + 16 * grp;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) S.k[j][ks] = load_stream(ks_src + 64 * ks);
-      }
-      // V, every format: the block's rows are contiguous; instruction i of lane l
-      // reads VB bytes of row crow(l) + i CROW_STEP at VB (l % CH), so each
-      // instruction covers whole rows, and the bytes widen to the chunk the
-      // lane stores.  Paged: a block has all 16 rows, so the loads are one
-      // address plus constant offsets, and rows past the sequence's length are
-      // zeroed after the load (compute).  Contiguous: rows past the length
-      // read its last row instead (the last stage may end past the capacity).
-      if constexpr (WV) {
-        // wide 8-bit: instruction i of lane l reads 16 bytes of row l / (RB / 16) +
-        // i 1024 / RB at 16 (l % (RB / 16)).  Rows past the length read its last
-        // row instead.
-        const int lim = min(kDecStage - 1, vlim);
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const int r = min(l / (RB / 16) + i * (1024 / RB), lim);
-          S.v[j][i] = load_stream_as<VT>(vp + (row0 + r) * RB + 16 * (l % (RB / 16)));
-        }
-      } else if constexpr (PAGED) {
-        const uint8_t* vs_src = vp + (row0 + Gm::crow(l)) * RB + VB * (l % Gm::CH);
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) S.v[j][i] = load_stream_as<VT>(vs_src + i * Gm::CROW_STEP * RB);
-      } else {
         const int lim = min(kDecStage - 1, vlim);
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
           const int r = min(Gm::crow(l) + i * Gm::CROW_STEP, lim);
-          S.v[j][i] = load_stream_as<VT>(vp + (row0 + r) * RB + VB * (l % Gm::CH));
+          S.v[j][i] = load_stream_as<VT>(vb + r * RB + VB * (l % Gm::CH));
         }
       }
     }
@@ -501,28 +468,89 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       const int gi = 16 * hg + col;
       const size_t qhead = (size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0);
       if constexpr (QS) {
-        // int8 digits of the scaled query (hi row, then lo row): k-step i of the
-        // int8 Q K^T takes the bytes the lane's keys give it: int8, bytes
-        // 64 i + 16 grp (as the K loads); int4, bytes D / 4 grp + 16 i (its keys'
-        // channels, in kI4ByteOrder)
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(qp) + qhead * 2 * D;
+        // the 16 consecutive channels qs_base(i) .. + 15 of k-step i, as loaded
+        // (the digits are made in compute), and the KV head's key scales into
+        // the next LDS slot (D floats, 16 bytes per lane)
+        const uint16_t* src = qp + qhead * D;
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) {
-          const int at = I4 ? (D / 4) * grp + 16 * i : 64 * i + 16 * grp;
-          S.q[2 * i] = *reinterpret_cast<const u32x4*>(src + at);
-          S.q[2 * i + 1] = *reinterpret_cast<const u32x4*>(src + D + at);
+          S.q[2 * i] = *reinterpret_cast<const u32x4*>(src + qs_base(i));
+          S.q[2 * i + 1] = *reinterpret_cast<const u32x4*>(src + qs_base(i) + 8);
         }
+        S.skslot = skslot;
+        skslot ^= 1;
+        if (l < D / 4)
+          lds_copy16(sa.k_scales + (size_t)g * D + 4 * l, lds_addr(sktile + (2 * w + S.skslot) * D));
       } else {
         const uint16_t* src = qp + qhead * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) S.q[ks] = *reinterpret_cast<const u32x4*>(src + qd(ks));
       }
-      if constexpr (QS) S.qfac = sa.q_fac[(size_t)c.b * a.H_q + g * G + (gi < G ? gi : 0)];
     }
   };
 
   // per-segment state
   u32x4 qf[KS];
+  // int8 / int4 caches: the key scales fold into the query, q'[c] = q[c] sk[c]
+  // in fp32.  Each head's q' is scaled so that its largest element is 32512
+  // and rounded to an integer x, held as two int8 digits x = 256 hi + lo (hi in
+  // [-127, 127], lo in [-128, 127]): Q K^T then runs on the int8 matrix cores,
+  // exactly (int32 sums), against the key codes.  x carries 15 bits and a
+  // sign.  qf[2 i] holds the hi digits of k-step i, qf[2 i + 1] the lo digits,
+  // byte p for channel qs_base(i) + p (int4: + kI4Channel(p)).  The four lanes
+  // of a head (grp 0..3) hold all its channels, so its maximum takes two lane
+  // exchanges.  Returns the factor that undoes the scaling in the logit scale:
+  // max |q'| / 32512, and a further 1/16 for the int4 cache, whose codes enter
+  // the products as bytes holding 16 times the code.
+  auto query_digits = [&](const Stage& S) {
+    // the key scales' copy was issued in this stage's load, before the next
+    // stage's K and V loads (kStageLoads of them, and perhaps more)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kStageLoads));
+    asm volatile("" ::: "memory");  // the LDS reads below stay after the wait
+    const float* skw = sktile + (2 * w + S.skslot) * D;
+    float v[D / 64][16];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const uint16_t* qh = reinterpret_cast<const uint16_t*>(&S.q[2 * i]);
+#pragma unroll
+      for (int p = 0; p < 16; p += 4) {
+        const f32x4 sk4 = *reinterpret_cast<const f32x4*>(skw + qs_base(i) + p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t b = qh[p + e];
+          v[i][p + e] = (std::is_same<T, BF16>::value ? bf16_bits_to_f32(b) : f16_bits_to_f32(b)) * sk4[e];
+          amax = fmaxf(amax, fabsf(v[i][p + e]));
+        }
+      }
+    }
+    amax = fmaxf(amax, xor_shfl(amax, 16));
+    amax = max_pair32(amax);
+    const float up = amax > 0.f ? 32512.f / amax : 0.f;
+    // rint(v up) lands in the low bits of fma(v, up, 1.5 * 2^23) (|v up| <= 32512
+    // < 2^22): byte 0 of those bits is lo, byte 1 of the bits plus 128 is hi
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      uint32_t t[16];
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int ch = I4 ? kI4Channel(p) : p;
+        t[p] = __float_as_uint(fmaf(v[i][ch], up, 12582912.f));
+      }
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t* u = t + 4 * d;
+        lo[d] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(u[3], u[2], 0x0c0c0400u),
+                                      __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u), 0x05040100u);
+        hi[d] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(u[3] + 128u, u[2] + 128u, 0x0c0c0501u),
+                                      __builtin_amdgcn_perm(u[1] + 128u, u[0] + 128u, 0x0c0c0501u), 0x05040100u);
+      }
+      qf[2 * i] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      qf[2 * i + 1] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    return amax * (1.f / 32512.f) * (I4 ? 0.0625f : 1.f);
+  };
   f32x4 oacc[DB];
   float m = kNegInf, lsum = 0.f, lexact = 0.f;
   int piece = 0;
@@ -572,9 +600,11 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     if (!S.ok && l == 0) raise_device_error(2);
     if (S.qnew) {
       // New segment: clear the running state and O.
+      if constexpr (QS)
+        cl = c_log2 * query_digits(S);
+      else
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = S.q[ks];
-      if constexpr (QS) cl = c_log2 * S.qfac;
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = S.q[ks];
       m = kNegInf;
       lsum = 0.f;
       lexact = 0.f;
@@ -603,7 +633,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
 #pragma unroll
         for (int j = 0; j < SB; ++j)
 #pragma unroll
-          for (int i = 0; i < VCH; ++i)
+          for (int i = 0; i < NV; ++i)
             vraw[j][i] = t0 + 16 * j + Gm::crow(l) + i * Gm::CROW_STEP < c.len ? vraw[j][i] : VT{};
       }
     }
@@ -615,7 +645,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
         // chunks 2 (l % (RB / 16)) and the next one (int8: the codes + 1152)
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-          const u32x2 w0 = u32x2{S.v[j][i][0], S.v[j][i][1]}, w1 = u32x2{S.v[j][i][2], S.v[j][i][3]};
+          const u32x2 w0 = u32x2{vraw[j][i][0], vraw[j][i][1]}, w1 = u32x2{vraw[j][i][2], vraw[j][i][3]};
           const u32x4 lo = I8 ? i8x8_to_f16_biased(w0) : fp8x8_to<T>(w0);
           const u32x4 hi = I8 ? i8x8_to_f16_biased(w1) : fp8x8_to<T>(w1);
           const int r = 16 * j + l / (RB / 16) + i * (1024 / RB), ch = 2 * (l % (RB / 16));
@@ -646,7 +676,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
         // cores: exact int32 sums, x = 256 hi + lo recombined exactly (each sum is
         // below 2^22 in magnitude), then fp32.  int8: the codes as stored (16 bytes
         // per k-step).  int4: each word of 8 codes unpacks to 8 bytes holding 16
-        // times the codes, even channels then odd (kI4ByteOrder), with one shift
+        // times the codes, even channels then odd (kI4Channel), with one shift
         // and two ANDs; the 1/16 is in the query's factor.
         i32x4 ahi = i32x4{0, 0, 0, 0}, alo = i32x4{0, 0, 0, 0};
 #pragma unroll
@@ -770,23 +800,23 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   load(ic, nblk, A);
   advance(ic);
   if (ic.pos < end) nblk = block_of(ic);
+  // One load call per half, its cursor selected: the compiler's wait counting
+  // then sees the next stage's loads issued on every path before the current
+  // stage's compute (with two call sites it also weighed a path through
+  // neither, and waited for every load before computing).
   for (int pos = beg; pos < end; pos += 2) {
+    load(pos + 1 < end ? ic : cc, nblk, B);
     if (pos + 1 < end) {
-      load(ic, nblk, B);
       advance(ic);
       if (ic.pos < end) nblk = block_of(ic);
-    } else {
-      load(cc, nblk, B);
     }
     compute(cc, A, pos + 1 == end);
     advance(cc);
     if (pos + 1 >= end) break;
+    load(pos + 2 < end ? ic : cc, nblk, A);
     if (pos + 2 < end) {
-      load(ic, nblk, A);
       advance(ic);
       if (ic.pos < end) nblk = block_of(ic);
-    } else {
-      load(cc, nblk, A);
     }
     compute(cc, B, pos + 2 == end);
     advance(cc);

@@ -53,17 +53,14 @@ def test_version_and_last_error():
 def test_workspace_bytes_host_logic():
     L = _lib_or_skip()
     # S = ceil(len / 256) + 1 partials per (b, h): fp32 outputs, then fp32 lse
-    # (each region 256-byte aligned), one int32 piece count per (b, h), then the
-    # integer caches' query digits int8 [B, H, 2, d] and fp32 factor per (b, h)
+    # (each region 256-byte aligned), then one int32 piece count per (b, h)
     def layout(B, H, cap, d):
         S = -(-cap // 256) + 1
         up = lambda x: -(-x // 256) * 256
         lse_off = up(B * H * S * d * 4)
         cnt_off = up(lse_off + B * H * S * 4)
-        qdig_off = up(cnt_off + B * H * 4)
-        qfac_off = up(qdig_off + B * H * 2 * d)
-        return qfac_off + B * H * 4
-    assert L.attn_decode_workspace_bytes(1, 1, 256, 128) == layout(1, 1, 256, 128) == 1024 + 256 + 256 + 256 + 4
+        return cnt_off + B * H * 4
+    assert L.attn_decode_workspace_bytes(1, 1, 256, 128) == layout(1, 1, 256, 128) == 1024 + 256 + 4
     assert L.attn_decode_workspace_bytes(32, 64, 32784, 128) == layout(32, 64, 32784, 128)
     assert L.attn_decode_workspace_bytes(3, 5, 1000, 64) == layout(3, 5, 1000, 64)
     assert L.attn_decode_workspace_bytes(0, 1, 1, 1) == 0
