@@ -10,17 +10,18 @@
 // Work split (persistent, balanced by bytes): the cache is cut into stages of
 // one segment = (sequence, KV head [x group of 16 query heads]); a stage is
 // one block of 16 tokens of a paged cache ("KV Cache:推理慢的真正原因",
-// 工程优化手段 / 1. PagedAttention), or four blocks of a 4-bit cache, so that a
-// stage holds as many bytes.  The stages of all segments, laid end to
+// 工程优化手段 / 1. PagedAttention), or two blocks of an int8 cache and four of
+// an int4 cache, so that a stage holds as many bytes.  The stages of all
+// segments, laid end to
 // end, form one stream; the grid is a fixed number of waves (as many as fit
 // on the GPU at once) and wave k takes an equal contiguous share of the
 // stream.  A wave never waits for another:
 //  * each stage's K rows are loaded straight into MFMA operand registers and
 //    its V rows into registers, the next stage's loads in flight while the
-//    current one is computed, across segment boundaries (16-byte loads with
-//    the non-temporal hint: they stream faster than global-to-LDS copies or
-//    ordinary loads on this part); the query
-//    rows of a segment are loaded with its first stage;
+//    current one is computed, across segment boundaries (loads with the
+//    non-temporal hint: they stream faster than global-to-LDS copies or
+//    ordinary loads on this part); the query rows of a segment are loaded
+//    with its first stage;
 //  * V goes through a wave-private LDS tile (16-bit values, 16 rows per
 //    block) to be read transposed; 8- and 4-bit values are widened on the way;
 //  * S^T = K Q^T (16 tokens x 16 query heads, heads beyond G are don't-care
@@ -29,9 +30,9 @@
 //    query's two int8 digits (made at each segment's start, query_digits);
 //  * running (max, sum) per head; the reference maximum only moves when a
 //    stage exceeds it by 2^8, so the O accumulator is rarely rescaled;
-//  * O^T += V^T P^T with v_mfma_f32_16x16x16: P^T comes straight from the S^T
-//    registers (rounded to 16 bits), V^T from ds_read_b64_tr_b16 on the
-//    row-major V stage.
+//  * O^T += V^T P^T with v_mfma_f32_16x16x16 (16x16x32 over two blocks when a
+//    stage has several): P^T comes straight from the S^T registers (rounded
+//    to 16 bits), V^T from ds_read_b64_tr_b16 on the row-major V stage.
 // Where a wave's share starts or ends inside a segment, or a segment ends, the
 // wave writes that piece's normalised partial output and lse (piece p of a
 // segment belongs to the p-th wave whose share overlaps it);
@@ -236,7 +237,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // bookkeeping) is spread over as many bytes and as many bytes are in flight.
   // The FP8 stage keeps one block: two measured about 1% slower there, against
   // about 2.5% faster for int8.
-  constexpr int SB = I4 ? 256 / RB : (I8 ? 256 / RB : 1);
+  constexpr int SB = QS ? 256 / RB : 1;
   constexpr int TS = kDecStage * SB;  // tokens per stage
   // vector memory instructions every stage's load issues (K, then V), before
   // any query row or key-scale copy
