@@ -337,9 +337,9 @@ int kv_append_int8(void* k_pool, void* v_pool, const void* k_new, const void* v_
 /* attn_decode_paged over the int8 pools: q, o [B, H_q, d] in `dtype` (F16 or
  * BF16), d = 64 or 128, scale > 0.  Same workspace as attn_decode_paged.
  * The scores are computed on the int8 matrix cores: the query times the key
- * scales, rescaled per head so that its largest element is 32512, is rounded
- * to an integer held as two int8 digits (16 bits with the sign), each
- * multiplied with the codes in exact int32 sums.
+ * scales, rescaled per head so that its largest element is 2^22 - 1, is
+ * rounded to an integer held as three int8 digits (23 bits with the sign),
+ * each multiplied with the codes in exact int32 sums.
  * Errors: as attn_decode_paged; INVALID_ARG for null or misaligned scale arrays;
  *         UNSUPPORTED for other dtypes / d. */
 int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool,

@@ -27,7 +27,7 @@
 //  * S^T = K Q^T (16 tokens x 16 query heads, heads beyond G are don't-care
 //    columns) with v_mfma_f32_16x16x32 on 16-bit and FP8 keys (FP8 widened in
 //    registers), or v_mfma_i32_16x16x64_i8 on int8 and int4 codes against the
-//    query's two int8 digits (made at each segment's start, query_digits);
+//    query's three int8 digits (made at each segment's start, query_digits);
 //  * running (max, sum) per head; the reference maximum only moves when a
 //    stage exceeds it by 2^8, so the O accumulator is rarely rescaled;
 //  * O^T += V^T P^T with v_mfma_f32_16x16x16 (16x16x32 over two blocks when a
@@ -188,6 +188,7 @@ constexpr float kI8Offset = 1152.f;  // widened int8 V values: code + 1152
 // 0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15.  The query's digits are
 // placed likewise.
 __device__ __forceinline__ constexpr int kI4Channel(int p) { return (p & 8) | ((p & 3) << 1) | ((p >> 2) & 1); }
+constexpr float kQTop = 4194303.f;  // 2^22 - 1: the largest |x| of a query's int8 digits
 
 // lens and table repeat sa.a.seq_lens and sa.a.table as restrict parameters:
 // nothing the kernel writes aliases them, so the compiler can read them with
@@ -493,18 +494,19 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   };
 
   // per-segment state
-  u32x4 qf[KS];
+  u32x4 qf[QS ? 3 * (D / 64) : KS];
   // int8 / int4 caches: the key scales fold into the query, q'[c] = q[c] sk[c]
-  // in fp32.  Each head's q' is scaled so that its largest element is 32512
-  // and rounded to an integer x, held as two int8 digits x = 256 hi + lo (hi in
-  // [-127, 127], lo in [-128, 127]): Q K^T then runs on the int8 matrix cores,
-  // exactly (int32 sums), against the key codes.  x carries 15 bits and a
-  // sign.  qf[2 i] holds the hi digits of k-step i, qf[2 i + 1] the lo digits,
-  // byte p for channel qs_base(i) + p (int4: + kI4Channel(p)).  The four lanes
-  // of a head (grp 0..3) hold all its channels, so its maximum takes two lane
-  // exchanges.  Returns the factor that undoes the scaling in the logit scale:
-  // max |q'| / 32512, and a further 1/16 for the int4 cache, whose codes enter
-  // the products as bytes holding 16 times the code.
+  // in fp32.  Each head's q' is scaled so that its largest element is kQTop =
+  // 2^22 - 1 and rounded to an integer x, held as three int8 digits x = 65536
+  // d2 + 256 d1 + d0: Q K^T then runs on the int8 matrix cores, exactly (int32
+  // sums), against the key codes.  x carries 22 bits and a sign, 2^-22 of the
+  // head's largest element (two digits, 15 bits, left errors of 3e-3 in the
+  // lse of heads with logits near 60).  qf[3 i .. 3 i + 2] hold d2, d1, d0 of
+  // k-step i, byte p for channel qs_base(i) + p (int4: + kI4Channel(p)).  The
+  // four lanes of a head (grp 0..3) hold all its channels, so its maximum
+  // takes two lane exchanges.  Returns the factor that undoes the scaling in
+  // the logit scale: max |q'| / kQTop, and a further 1/16 for the int4 cache,
+  // whose codes enter the products as bytes holding 16 times the code.
   auto query_digits = [&](const Stage& S) {
     // the key scales' copy was issued in this stage's load, before the next
     // stage's K and V loads (kStageLoads of them, and perhaps more)
@@ -529,9 +531,22 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     }
     amax = fmaxf(amax, xor_shfl(amax, 16));
     amax = max_pair32(amax);
-    const float up = amax > 0.f ? 32512.f / amax : 0.f;
-    // rint(v up) lands in the low bits of fma(v, up, 1.5 * 2^23) (|v up| <= 32512
-    // < 2^22): byte 0 of those bits is lo, byte 1 of the bits plus 128 is hi
+    // A head whose largest |q'| is at most 1e-30 (an all-zero query, in
+    // practice) gets zero digits: its true scores are below 1e-27 in magnitude,
+    // zero to within fp32 rounding of the softmax.  This also keeps 32512 / amax
+    // finite and the returned factor positive, so that a masked score (-inf)
+    // times the logit scale stays -inf rather than becoming -inf * 0 = NaN.
+    const bool live = amax > 1e-30f;
+    const float up = live ? kQTop / amax : 0.f;
+    // rint(v up) = x lands in the low bits of fma(v, up, 1.5 * 2^23): the bits are
+    // 0x4B400000 + x for |x| <= 2^22 (the binade [2^23, 2^24) has spacing 1).
+    // x = 65536 d2 + 256 d1 + d0 with d0, d1 in [-128, 127] and d2 in [-64, 64]:
+    // d0 is byte 0 of x, d1 byte 1 of x + 128, d2 byte 2 of x + 32896, each read
+    // as a two's-complement byte (the constant's bytes 0 and 1 are zero).
+    const auto byte = [](const uint32_t* u, uint32_t add, uint32_t sel) {
+      return __builtin_amdgcn_perm(__builtin_amdgcn_perm(u[3] + add, u[2] + add, sel),
+                                   __builtin_amdgcn_perm(u[1] + add, u[0] + add, sel), 0x05040100u);
+    };
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
       uint32_t t[16];
@@ -540,19 +555,18 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
         const int ch = I4 ? kI4Channel(p) : p;
         t[p] = __float_as_uint(fmaf(v[i][ch], up, 12582912.f));
       }
-      uint32_t hi[4], lo[4];
+      uint32_t d2[4], d1[4], d0[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t* u = t + 4 * d;
-        lo[d] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(u[3], u[2], 0x0c0c0400u),
-                                      __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u), 0x05040100u);
-        hi[d] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(u[3] + 128u, u[2] + 128u, 0x0c0c0501u),
-                                      __builtin_amdgcn_perm(u[1] + 128u, u[0] + 128u, 0x0c0c0501u), 0x05040100u);
+        d0[d] = byte(t + 4 * d, 0u, 0x0c0c0400u);
+        d1[d] = byte(t + 4 * d, 128u, 0x0c0c0501u);
+        d2[d] = byte(t + 4 * d, 32896u - 0x4B400000u, 0x0c0c0602u);
       }
-      qf[2 * i] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      qf[2 * i + 1] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      qf[3 * i] = u32x4{d2[0], d2[1], d2[2], d2[3]};
+      qf[3 * i + 1] = u32x4{d1[0], d1[1], d1[2], d1[3]};
+      qf[3 * i + 2] = u32x4{d0[0], d0[1], d0[2], d0[3]};
     }
-    return amax * (1.f / 32512.f) * (I4 ? 0.0625f : 1.f);
+    return live ? amax * (1.f / kQTop) * (I4 ? 0.0625f : 1.f) : 1.f;
   };
   f32x4 oacc[DB];
   float m = kNegInf, lsum = 0.f, lexact = 0.f;
@@ -675,13 +689,13 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       }
       sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (QS) {
-        // the key codes against the query's two int8 digits on the int8 matrix
-        // cores: exact int32 sums, x = 256 hi + lo recombined exactly (each sum is
-        // below 2^22 in magnitude), then fp32.  int8: the codes as stored (16 bytes
+        // the key codes against the query's three int8 digits on the int8 matrix
+        // cores: exact int32 sums (each below 2^22 in magnitude), 256 S1 + S0
+        // exact in int32, then 65536 S2 added in fp32 (one rounding).  int8: the codes as stored (16 bytes
         // per k-step).  int4: each word of 8 codes unpacks to 8 bytes holding 16
         // times the codes, even channels then odd (kI4Channel), with one shift
         // and two ANDs; the 1/16 is in the query's factor.
-        i32x4 ahi = i32x4{0, 0, 0, 0}, alo = i32x4{0, 0, 0, 0};
+        i32x4 a2 = i32x4{0, 0, 0, 0}, a1 = i32x4{0, 0, 0, 0}, a0 = i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) {
           u32x4 kb;
@@ -691,11 +705,12 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
           } else {
             kb = S.k[j][i];
           }
-          ahi = mfma16k64_i8(kb, qf[2 * i], ahi);
-          alo = mfma16k64_i8(kb, qf[2 * i + 1], alo);
+          a2 = mfma16k64_i8(kb, qf[3 * i], a2);
+          a1 = mfma16k64_i8(kb, qf[3 * i + 1], a1);
+          a0 = mfma16k64_i8(kb, qf[3 * i + 2], a0);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[j][e] = (float)(ahi[e] * 256 + alo[e]);
+        for (int e = 0; e < 4; ++e) sacc[j][e] = fmaf((float)a2[e], 65536.f, (float)(a1[e] * 256 + a0[e]));
       } else if constexpr (Q8) {
         // FP8 K: 16 bytes per load, widened into two k-steps
 #pragma unroll

@@ -62,9 +62,11 @@ def test_int8_append_image_is_bit_exact(K, dtype, pow2):
     assert vp.cpu().numpy().tobytes() == cache.v.tobytes(), "V pool image differs"
 
 
-def run_int8(K, case, lens=None, heads=None, poison=False):
+def run_int8(K, case, lens=None, heads=None, poison=False, edit=None):
     print(f"[int8] {case}", flush=True)
     inp = synth.int8_decode_inputs(case, lens=lens)
+    if edit is not None:
+        edit(inp, case.dtype)
     dt = case.dtype
     lens_d = to_dev_i32(inp["lens"])
     kp, vp = i8(inp["k_pool"]), i8(inp["v_pool"])
@@ -155,9 +157,11 @@ def u8(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).cuda()
 
 
-def run_int4(K, case, lens=None, heads=None, poison=False):
+def run_int4(K, case, lens=None, heads=None, poison=False, edit=None):
     print(f"[int4] {case}", flush=True)
     inp = synth.int4_decode_inputs(case, lens=lens)
+    if edit is not None:
+        edit(inp, case.dtype)
     dt = case.dtype
     lens_d = to_dev_i32(inp["lens"])
     kp, vp = u8(inp["k_pool"]), u8(inp["v_pool"])
@@ -229,3 +233,34 @@ def test_int4_decode_stage_tails_read_no_table_entry_past_the_length(K, d):
 def test_int8_decode_reads_no_table_entry_past_the_length(K, d):
     run_int8(K, synth.DecodeCase("i8", len(STAGE_TAIL_LENS), 8, 2, d, "f16", 0, 260, True, 290 + d),
              lens=STAGE_TAIL_LENS, poison=True)
+
+
+def extreme_queries(inp, dtype):
+    """Query heads that stress the query's int8 digits (the key scales folded in,
+    each head scaled to its largest element and rounded to 16 bits): an all-zero
+    head, one dominant channel over tiny ones, a head of tiny values, a head of
+    large values, and key scales of zero on some channels."""
+    bits = inp["q"]  # [B, H_q, d] storage bits
+    if dtype == "bf16":
+        q = (bits.astype(np.uint32) << 16).view(np.float32).copy()
+    else:
+        q = bits.view(np.float16).astype(np.float32)
+    q[:, 0, :] = 0.0
+    q[:, 1, :] = 1e-3 * np.sign(q[:, 1, :])
+    q[:, 1, 5] = 8.0
+    q[:, 2, :] = q[:, 2, :] * 1e-20
+    q[:, 3, :] = q[:, 3, :] * 40.0
+    inp["q"] = synth.to_storage(q, dtype)
+    ks = inp["k_scales"].copy()
+    ks[:, ::7] = 0.0
+    inp["k_scales"] = ks
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_int8_decode_extreme_queries(K, d):
+    run_int8(K, synth.DecodeCase("i8", 4, 8, 2, d, "bf16", 1, 300, True, 300 + d), edit=extreme_queries)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_int4_decode_extreme_queries(K, d):
+    run_int4(K, synth.DecodeCase("i4", 4, 8, 2, d, "f16", 1, 300, True, 310 + d), edit=extreme_queries)
