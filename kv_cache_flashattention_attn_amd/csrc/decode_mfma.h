@@ -532,7 +532,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     amax = fmaxf(amax, xor_shfl(amax, 16));
     amax = max_pair32(amax);
     // A head whose largest |q'| is at most 1e-30 (an all-zero query, in
-    // practice) gets zero digits: its true scores are below 1e-27 in magnitude,
+    // practice) gets zero digits: its true scores (q' times the codes, at most 127 in magnitude) are below 2e-26,
     // zero to within fp32 rounding of the softmax.  This also keeps kQTop / amax
     // finite and the returned factor positive, so that a masked score (-inf)
     // times the logit scale stays -inf rather than becoming -inf * 0 = NaN.
