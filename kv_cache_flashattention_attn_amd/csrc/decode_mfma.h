@@ -532,10 +532,11 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     amax = fmaxf(amax, xor_shfl(amax, 16));
     amax = max_pair32(amax);
     // A head whose largest |q'| is at most 1e-30 (an all-zero query, in
-    // practice) gets zero digits: its true scores (q' times the codes, at most 127 in magnitude) are below 2e-26,
-    // zero to within fp32 rounding of the softmax.  This also keeps kQTop / amax
-    // finite and the returned factor positive, so that a masked score (-inf)
-    // times the logit scale stays -inf rather than becoming -inf * 0 = NaN.
+    // practice) gets zero digits: its true scores (q' times codes of at most
+    // 127 in magnitude, over d channels) are below 2e-26, zero to within fp32
+    // rounding of the softmax.  This also keeps kQTop / amax finite and the
+    // returned factor positive, so that a masked score (-inf) times the logit
+    // scale stays -inf rather than becoming -inf * 0 = NaN.
     const bool live = amax > 1e-30f;
     const float up = live ? kQTop / amax : 0.f;
     // rint(v up) = x lands in the low bits of fma(v, up, 1.5 * 2^23): the bits are
