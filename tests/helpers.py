@@ -109,3 +109,28 @@ def poison_table_tail(table, lens, num_blocks):
         used = -(-int(lens[b]) // 16)
         t[b, used:] = -7 if b % 2 == 0 else num_blocks + 1000
     return t
+
+
+def extreme_queries(inp, dtype):
+    """Edit decode inputs in place so that query heads stress the score path: an
+    all-zero head, one dominant channel over tiny ones, a head of tiny values and
+    a head of large values (logits near 60); with per-channel key scales, the
+    scales of every 7th channel are set to zero as well."""
+    import synth
+    bits = inp["q"]  # [B, H_q, d] storage bits
+    if dtype == "bf16":
+        q = (bits.astype(np.uint32) << 16).view(np.float32).copy()
+    elif dtype == "f16":
+        q = bits.view(np.float16).astype(np.float32)
+    else:
+        q = np.array(bits, dtype=np.float32)
+    q[:, 0, :] = 0.0
+    q[:, 1, :] = 1e-3 * np.sign(q[:, 1, :])
+    q[:, 1, 5] = 8.0
+    q[:, 2, :] = q[:, 2, :] * 1e-20
+    q[:, 3, :] = q[:, 3, :] * 40.0
+    inp["q"] = synth.to_storage(q, dtype)
+    if "k_scales" in inp:
+        ks = inp["k_scales"].copy()
+        ks[:, ::7] = 0.0
+        inp["k_scales"] = ks

@@ -4,7 +4,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_close, assert_lse_close, assert_stored_output, bits_of, to_dev, to_dev_i32, values_of
+from helpers import (assert_close, assert_lse_close, assert_stored_output, bits_of, extreme_queries, to_dev,
+                     to_dev_i32, values_of)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -284,3 +285,14 @@ def test_oracle_catches_a_corrupted_block_table(K):
     Oref, _ = oracle.decode_step(pc, inp["q"], empty, empty, seq, c.sm_scale, dt)
     err = np.abs(values_of(o)[0] - Oref[0]).max()
     assert err > 1e-2
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_decode_extreme_queries(K, paged, dtype):
+    """Query heads that are all zero, one dominant channel over tiny ones, tiny,
+    or large (logits near 60)."""
+    c = case(paged, 4, 8, 2, 128, dtype, 1, 300, 330 + paged)
+    inp = synth.decode_inputs(c)
+    extreme_queries(inp, dtype)
+    run_step(K, c, inp=inp)

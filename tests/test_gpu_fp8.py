@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import poison_table_tail, assert_lse_close, assert_stored_output, to_dev, to_dev_i32
+from helpers import extreme_queries, poison_table_tail, assert_lse_close, assert_stored_output, to_dev, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -52,12 +52,14 @@ def test_fp8_append_image_is_bit_exact(K, dtype, scales):
     assert vp.cpu().numpy().tobytes() == cache.v.tobytes(), "V pool image differs"
 
 
-def run_fp8(K, case, lens=None, ks=synth.FP8_K_SCALE, vs=synth.FP8_V_SCALE, heads=None, poison=False):
+def run_fp8(K, case, lens=None, ks=synth.FP8_K_SCALE, vs=synth.FP8_V_SCALE, heads=None, poison=False, edit=None):
     """Append + decode over pools of every finite E4M3 code (empty slots hold NaN
     codes), checked with the stored-output rule: the fp32-output call meets the
     bar, the 16-bit output is its round-to-nearest-even."""
     print(f"[fp8] {case} k_scale={ks} v_scale={vs}", flush=True)
     inp = synth.fp8_decode_inputs(case, lens=lens)
+    if edit is not None:
+        edit(inp, case.dtype)
     dt = case.dtype
     lens_d = to_dev_i32(inp["lens"])
     kp, vp = u8(inp["k_pool"]), u8(inp["v_pool"])
@@ -124,3 +126,10 @@ def test_fp8_bad_block_raises_flag(K):
 def test_fp8_decode_reads_no_table_entry_past_the_length(K, d):
     lens = np.array([0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 127, 128, 250], dtype=np.int32)
     run_fp8(K, synth.DecodeCase("f8", len(lens), 8, 2, d, "bf16", 0, 260, True, 300 + d), lens=lens, poison=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fp8_decode_extreme_queries(K, dtype):
+    """Query heads that are all zero, one dominant channel over tiny ones, tiny,
+    or large, over the FP8 cache."""
+    run_fp8(K, synth.DecodeCase("f8x", 4, 8, 2, 128, dtype, 1, 300, True, 340 + len(dtype)), edit=extreme_queries)

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import poison_table_tail, assert_lse_close, assert_stored_output, to_dev, to_dev_i32
+from helpers import extreme_queries, poison_table_tail, assert_lse_close, assert_stored_output, to_dev, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -233,27 +233,6 @@ def test_int4_decode_stage_tails_read_no_table_entry_past_the_length(K, d):
 def test_int8_decode_reads_no_table_entry_past_the_length(K, d):
     run_int8(K, synth.DecodeCase("i8", len(STAGE_TAIL_LENS), 8, 2, d, "f16", 0, 260, True, 290 + d),
              lens=STAGE_TAIL_LENS, poison=True)
-
-
-def extreme_queries(inp, dtype):
-    """Query heads that stress the query's int8 digits (the key scales folded in,
-    each head scaled to its largest element and rounded to 16 bits): an all-zero
-    head, one dominant channel over tiny ones, a head of tiny values, a head of
-    large values, and key scales of zero on some channels."""
-    bits = inp["q"]  # [B, H_q, d] storage bits
-    if dtype == "bf16":
-        q = (bits.astype(np.uint32) << 16).view(np.float32).copy()
-    else:
-        q = bits.view(np.float16).astype(np.float32)
-    q[:, 0, :] = 0.0
-    q[:, 1, :] = 1e-3 * np.sign(q[:, 1, :])
-    q[:, 1, 5] = 8.0
-    q[:, 2, :] = q[:, 2, :] * 1e-20
-    q[:, 3, :] = q[:, 3, :] * 40.0
-    inp["q"] = synth.to_storage(q, dtype)
-    ks = inp["k_scales"].copy()
-    ks[:, ::7] = 0.0
-    inp["k_scales"] = ks
 
 
 @pytest.mark.parametrize("d", [64, 128])
