@@ -95,7 +95,7 @@ def test_fp8_decode_chunk_boundaries(K, d, dtype):
     run_fp8(K, synth.DecodeCase("fp8", len(lens), 8, 2, d, dtype, 0, 1600, True, 110 + d), lens=lens)
 
 
-@pytest.mark.parametrize("G", [1, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 4, 8, 16, 24, 32])
 def test_fp8_decode_gqa_groups(K, G):
     run_fp8(K, synth.DecodeCase("fp8", 3, 2 * G, 2, 128, "bf16", 1, 700, True, 120 + G))
 

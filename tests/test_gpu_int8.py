@@ -100,7 +100,7 @@ def test_int8_decode_chunk_boundaries(K, d, dtype):
     run_int8(K, synth.DecodeCase("i8", len(lens), 8, 2, d, dtype, 0, 1600, True, 210 + d), lens=lens)
 
 
-@pytest.mark.parametrize("G", [1, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 4, 8, 16, 24, 32])
 def test_int8_decode_gqa_groups(K, G):
     run_int8(K, synth.DecodeCase("i8", 3, 2 * G, 2, 128, "bf16", 1, 700, True, 220 + G))
 
@@ -195,7 +195,7 @@ def test_int4_decode_chunk_boundaries(K, d, dtype):
     run_int4(K, synth.DecodeCase("i4", len(lens), 8, 2, d, dtype, 0, 1600, True, 250 + d), lens=lens)
 
 
-@pytest.mark.parametrize("G", [1, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 4, 8, 16, 24, 32])
 def test_int4_decode_gqa_groups(K, G):
     run_int4(K, synth.DecodeCase("i4", 3, 2 * G, 2, 128, "bf16", 1, 700, True, 260 + G))
 
@@ -243,3 +243,12 @@ def test_int8_decode_extreme_queries(K, d):
 @pytest.mark.parametrize("d", [64, 128])
 def test_int4_decode_extreme_queries(K, d):
     run_int4(K, synth.DecodeCase("i4", 4, 8, 2, d, "f16", 1, 300, True, 310 + d), edit=extreme_queries)
+
+
+def test_int8_decode_two_head_groups_d64(K):
+    """G = 24 at d = 64: two groups of query heads per KV head, the second partly filled."""
+    run_int8(K, synth.DecodeCase("i8", 3, 48, 2, 64, "f16", 1, 700, True, 350))
+
+
+def test_int4_decode_two_head_groups_d64(K):
+    run_int4(K, synth.DecodeCase("i4", 3, 48, 2, 64, "f16", 1, 700, True, 351))
