@@ -105,3 +105,35 @@ def test_quantised_decode_poisoned_buffers(K, fmt):
         app(kp, vp, kn, vn, lens, tb, ks, vs)
         fn = lambda **kw: dec(q, kp, vp, tb, seq, ks, vs, scale=c.sm_scale, **kw)  # noqa: E731
     check_decode(K, fn, q, ws, (c.B, c.H_q))
+
+
+def test_chunk_prefill_poisoned_outputs(K):
+    c = synth.DecodeCase("poison", 4, 8, 2, 128, "bf16", 0, 400, True, 430, n_new=70)
+    inp = synth.chunk_inputs(c)
+    lens = to_dev_i32(inp["lens"])
+    q = to_dev(inp["q"], "bf16")
+    kp, vp = to_dev(inp["k_pool"], "bf16"), to_dev(inp["v_pool"], "bf16")
+    tb = to_dev_i32(inp["block_table"])
+    K.kv_append(kp, vp, to_dev(inp["k_new"], "bf16"), to_dev(inp["v_new"], "bf16"), lens, tb)
+    o0, l0 = K.attn_prefill_paged(q, kp, vp, tb, lens, scale=c.sm_scale, return_lse=True)
+    o1, l1 = K.attn_prefill_paged(q, kp, vp, tb, lens, scale=c.sm_scale, return_lse=True, out=nan_like(o0),
+                                  lse=nan_like(l0))
+    torch.cuda.synchronize()
+    assert K.attn_device_error_flags() == 0
+    same(o0, o1, "O")
+    same(l0, l1, "lse")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_prefill_poisoned_outputs(K, causal):
+    pc = synth.PrefillCase("poison", 1, 4, 2, 300, 128, "bf16", causal, True, 440 + causal)
+    inp = synth.fp8_prefill_inputs(pc)
+    q8, k8, v8 = (torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.uint8)).cuda() for n in ("q", "k", "v"))
+    kw = dict(causal=causal, scale=pc.sm_scale, q_scale=synth.FP8_Q_SCALE, k_scale=synth.FP8_K_SCALE,
+              v_scale=synth.FP8_V_SCALE)
+    o0, l0 = K.attn_prefill_fp8(q8, k8, v8, return_lse=True, **kw)
+    o1, l1 = K.attn_prefill_fp8(q8, k8, v8, return_lse=True, out=nan_like(o0), lse=nan_like(l0), **kw)
+    torch.cuda.synchronize()
+    assert K.attn_device_error_flags() == 0
+    same(o0, o1, "O")
+    same(l0, l1, "lse")
