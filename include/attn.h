@@ -17,7 +17,11 @@
  *    allocates, frees or keeps a pointer after a call returns.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
  *    Calls are asynchronous and never synchronise, except
- *    attn_device_error_flags().
+ *    attn_device_error_flags().  The compute calls launch kernels only (no
+ *    allocation, no memset, no copy), so a stream under HIP graph capture may
+ *    record them; a replay repeats exactly what the call did.  Make one eager
+ *    call of each kind before capturing (the first decode call also sizes its
+ *    persistent grid from an occupancy query).
  *  - dtype is one of ATTN_F32, ATTN_F16, ATTN_BF16; Q, K, V, caches and the
  *    output share it (unless out_fp32 asks for an fp32 output).  lse outputs
  *    are always fp32, natural log.
