@@ -68,6 +68,19 @@ def test_gqa_prefill(K, G, causal):
     run_case(K, 3100 + G, 1, 2 * G, 2, 77, 16, "f32", causal)
 
 
+@pytest.mark.parametrize("B,H_q,H_kv,N", [(1, 8, 8, 512), (1, 24, 8, 384), (3, 8, 2, 256), (1, 12, 4, 256),
+                                          (2, 16, 4, 512), (1, 3, 1, 300)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_block_orders(K, B, H_q, H_kv, N, causal):
+    """Shapes that take every branch of the workgroup order (128-row query blocks,
+    8 XCDs): blocks a multiple of 8 or not; causal with whole heads per XCD in
+    groups of two (2, 16, 4, 512) or one (odd heads per XCD: 1 of 8 x 512,
+    3 of 24 x 384, 3 of 3 x 8 x 256); causal with a per-XCD count that is not a
+    multiple of the query blocks (1 x 12 x 256); the plain order (1 x 3 x 300).
+    Every query block must be computed once, with its own head's K and V."""
+    run_case(K, 5000 + B * H_q + N, B, H_q, H_kv, N, 128, "bf16", causal)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_gqa_small_noncausal_d64(K, dtype):
     """Small non-causal d = 64 problems take the key-split kernel: GQA head mapping
