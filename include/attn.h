@@ -228,11 +228,19 @@ int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_p
  *
  * Same per-channel scales and rounding as kv_append_int8 with codes clamped to
  * [-7, 7] (int4 caches: "KV Cache:推理慢的真正原因", 工程优化手段, the
- * quantization item), two codes per byte: element 2i in the low nibble,
- * element 2i + 1 in the high nibble, each 4-bit two's complement.  The pools
- * are bytes [num_blocks, H_kv, 16, d / 2]; a nibble holding -8 (never written
- * by kv_append_int4) decodes to -8.  Arguments, errors and workspace as for the
- * int8 calls; attn_decode_paged_int4 takes f16 / bf16 queries at d = 64 or 128.
+ * quantization item), two codes per byte, each 4-bit two's complement.  The
+ * pools are bytes [num_blocks, H_kv, 16, d / 2].
+ *  - K: row t of a block is token t, element 2i in the low nibble and element
+ *    2i + 1 in the high nibble.
+ *  - V: the 8 d bytes of a (block, KV head) are in the order the decode's
+ *    P V matrix product reads them: 64 runs of d / 8 bytes; run 16 g + i holds
+ *    tokens 4 g .. 4 g + 3 of channels i, i + 16, i + 32, ...; byte 4 w + j of
+ *    a run holds token 4 g + (0, 2, 1, 3)[j] of channel 32 w + i (low nibble)
+ *    and of channel 32 w + 16 + i (high nibble).  A byte holds one token.
+ * A nibble holding -8 (never written by kv_append_int4) decodes to -8.  d must
+ * be a multiple of 32 (UNSUPPORTED otherwise).  Arguments, errors and
+ * workspace as for the int8 calls; attn_decode_paged_int4 takes f16 / bf16
+ * queries at d = 64 or 128.
  */
 int kv_append_int4(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                    const int32_t* cache_lens, const int32_t* block_table,

@@ -639,6 +639,8 @@ int append_8bit(const char* fn, int mode, void* k_pool, void* v_pool, const void
   if (!valid_dtype(dtype)) return fail(ATTN_ERR_UNSUPPORTED, "%s: dtype %d not supported", fn, dtype);
   if (!plain_head_dim(d)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d not supported", fn, d);
   if (block_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "%s: block_size must be 16 (got %d)", fn, block_size);
+  if (mode == 2 && d % 32 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d not supported (int4 V pairs channel groups: d % 32 == 0)", fn, d);
   if (max_blocks_per_seq < 1 || num_blocks < 1)
     return fail(ATTN_ERR_INVALID_ARG, "%s: max_blocks_per_seq and num_blocks must be >= 1", fn);
   const bool i8 = mode != 0;
@@ -654,7 +656,7 @@ int append_8bit(const char* fn, int mode, void* k_pool, void* v_pool, const void
   attn::Append8Args a{static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_new, v_new, cache_lens,
                       block_table, B, H_kv, n_new, d, max_blocks_per_seq, num_blocks,
                       i8 ? 1.f : 1.0f / k_scale, i8 ? 1.f : 1.0f / v_scale, k_scales, v_scales};
-  const long long threads = (long long)B * H_kv * n_new * (d / (mode == 2 ? 16 : 8));
+  const long long threads = (long long)B * H_kv * n_new * (d / (mode == 2 ? 32 : 8));
   const dim3 grid((unsigned)((threads + 255) / 256));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (mode == 2) {

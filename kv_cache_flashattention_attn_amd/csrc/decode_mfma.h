@@ -23,7 +23,9 @@
 //    ordinary loads on this part); the query rows of a segment are loaded
 //    with its first stage;
 //  * V goes through a wave-private LDS tile (16-bit values, 16 rows per
-//    block) to be read transposed; 8- and 4-bit values are widened on the way;
+//    block) to be read transposed, 8-bit values widened on the way; the int4
+//    cache stores V in the P V operand's order, so its V is loaded straight
+//    into registers and widened there (no LDS tile);
 //  * S^T = K Q^T (16 tokens x 16 query heads, heads beyond G are don't-care
 //    columns) with v_mfma_f32_16x16x32 on 16-bit and FP8 keys (FP8 widened in
 //    registers), or v_mfma_i32_16x16x64_i8 on int8 and int4 codes against the
@@ -102,8 +104,7 @@ struct DecGeom {
   // part with the LDS bank-conflict counter, this is conflict-free, while
   // stores in which neighbouring lanes write chunks that are not neighbours
   // (every second or fourth chunk of a row) are not, whatever the XOR.  So the
-  // 8- and 4-bit stages load 8 or 4 bytes per lane, which widen to exactly
-  // this one chunk.
+  // 8-bit stages rotate their chunks (vchunk) to the same effect.
   static __device__ __forceinline__ int crow(int l) { return l / CH; }
   static constexpr int CROW_STEP = 1024 / ROWB;
 };
@@ -142,30 +143,22 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
-// 8 int4 codes (one word: byte b holds elements 2b (low nibble) and 2b + 1)
-// -> 8 biased f16 values in the order e0, e4, e1, e5, e2, e6, e3, e7 (element e
-// in 16-bit slot kI4Slot(e)).  With u = code + 8 (the nibble XOR 8), each 16-bit
-// half of a word takes one nibble with one three-input bit operation that also
-// applies the XOR: the f16 with bits 0x6400 | u is 1024 + u and the one with
-// 0x6400 | (u << 4) is 1024 + 16 u, exactly.  The V path keeps these biased
-// values and removes the bias once from the normalised output, per slot: a value
-// v holds code c as 1024 + (c + 8) in slots 0, 1, 4, 5, so c = v - kI4RawOff,
-// and as 1024 + 16 (c + 8) in slots 2, 3, 6, 7, so c = (v - kI4RawOff16) / 16.
-// The output rows are written back in channel order.
-__device__ __forceinline__ constexpr int kI4Slot(int e) { return ((e & 3) << 1) | (e >> 2); }
-constexpr float kI4RawOff = 1032.f, kI4RawOff16 = 1152.f;
-__device__ __forceinline__ u32x4 i4x8_to_f16_biased(uint32_t w) {
-  // ((w ^ 0x88888888) & mask) | 0x64006400 = (w & mask) ^ ((0x88888888 & mask) | 0x64006400),
-  // since the mask's bits and 0x64006400's are disjoint: one v_bitop3_b32 each
-  // (truth table 0x6A = (S0 & S1) ^ S2), the bias folded into the constant
-  auto pick = [](uint32_t x, uint32_t mask) -> uint32_t {
-    return __builtin_amdgcn_bitop3_b32(x, mask, (0x88888888u & mask) | 0x64006400u, 0x6A);
-  };
-  const uint32_t x2 = w >> 8;
-  return u32x4{pick(w, 0x000F000Fu),    // 1024 + u0, 1024 + u4
-               pick(w, 0x00F000F0u),    // 1024 + 16 u1, 1024 + 16 u5
-               pick(x2, 0x000F000Fu),   // 1024 + u2, 1024 + u6
-               pick(x2, 0x00F000F0u)};  // 1024 + 16 u3, 1024 + 16 u7
+// int4 V in the pool's operand order (kv_append_int4_kernel): lane (i, g) of a
+// block's d * 8 bytes loads its run of d / 8 bytes, tokens 4 g .. 4 g + 3 of
+// channels i + 16 m; word w holds channel groups m = 2 w (low nibbles) and
+// 2 w + 1 (high nibbles), its bytes tokens 0, 2, 1, 3 of the four.  The P V
+// operand of channel group m is the four tokens' values in order, two f16 per
+// word: tokens 0 and 1 are nibbles 0 and 4 of the word (m even; 1 and 5 for m
+// odd), tokens 2 and 3 nibbles 2 and 6 (3 and 7).  With u = code + 8 (the
+// nibble XOR 8), one three-input bit operation per f16 pair takes the two
+// nibbles shifted to bits 0 and 16 and makes 0x6400 | u, i.e. 1024 + u exactly:
+// ((y & 0x000F000F) ^ 0x64086408), truth table 0x6A = (S0 & S1) ^ S2.  V then
+// carries the codes + kI4VOffset, removed once from the normalised output.
+constexpr float kI4VOffset = 1032.f;
+__device__ __forceinline__ u32x2 i4_v_operand(uint32_t x, int m) {
+  const int sh = (m & 1) * 4;
+  auto pick = [](uint32_t y) -> uint32_t { return __builtin_amdgcn_bitop3_b32(y, 0x000F000Fu, 0x64086408u, 0x6A); };
+  return u32x2{pick(x >> sh), pick(x >> (sh + 8))};
 }
 
 // 8 int8 codes (words w[0..1]) -> 8 biased f16 values.  After the XOR with 0x80
@@ -209,14 +202,13 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // bytes per cache row, and 16-byte pieces of K and of V a lane loads per stage
   constexpr int RB = I4 ? D / 2 : (Q8 ? D : ROWB);
   constexpr int NKL = I4 ? 1 : (Q8 ? D / 64 : KS);
-  // V loads of an 8- or 4-bit cache.  Narrow (4-bit, WV false): VCH loads per
-  // lane per block of VB = 4 bytes, each widening to one 16-byte chunk of the
-  // LDS tile, in the 16-bit stores' conflict-free order.  Wide (8-bit, WV
-  // true): the 16-bit path's 16-byte loads, each widening to two chunks of one
-  // row, stored in the rotated chunk order (vchunk).
+  // V loads of an 8- or 4-bit cache.  Wide (8-bit, WV true): the 16-bit
+  // path's 16-byte loads, each widening to two chunks of one row, stored in the
+  // rotated chunk order (vchunk).  4-bit: one load per lane per block of its
+  // run of VB = D / 8 bytes, already in P V operand order (no LDS tile).
   constexpr bool WV = Q8 && !I4;
-  constexpr int VB = !Q8 ? 16 : WV ? 16 : 4;
-  constexpr int NV = WV ? D / 64 : VCH;  // V loads per lane per block
+  constexpr int VB = I4 ? D / 8 : 16;
+  constexpr int NV = WV ? D / 64 : I4 ? 1 : VCH;  // V loads per lane per block
   using VT = typename std::conditional<VB == 16, u32x4,
                                        typename std::conditional<VB == 8, u32x2, uint32_t>::type>::type;
   // Physical 16-byte chunk of logical chunk c of tile row r.  The wide 8-bit
@@ -245,7 +237,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   constexpr int kStageLoads = SB * (NKL + NV);
   static_assert(!Q8 || PAGED, "8- and 4-bit caches are paged");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t vtile[kDecWaves * Gm::SLOT * SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vtile[I4 ? 16 : kDecWaves * Gm::SLOT * SB];
   // int8 / int4: two slots per wave for the key scales of a segment's KV head,
   // copied from global memory with the stage that starts the segment
   __shared__ __attribute__((aligned(16))) float sktile[QS ? kDecWaves * 2 * D : 1];
@@ -282,12 +274,13 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // 64 i) of row col, so one instruction covers 64 contiguous bytes of every
   // row (the query fragments use the same assignment of d to k-steps, qd);
   // 4-bit rows, D / 8 bytes at D / 8 grp (one 16-byte load at d = 128, 8 bytes
-  // at d = 64).  V (16-bit and 4-bit): VB bytes of row crow(l) + i CROW_STEP at
-  // VB (l % CH), so each instruction covers whole rows and the bytes widen to
-  // the chunk the lane stores; the wide 8-bit loads take 16 bytes of row
-  // l / (RB / 16) + i 1024 / RB at 16 (l % (RB / 16)) (in load).
+  // at d = 64).  V: 16-bit rows, 16 bytes of row crow(l) + i CROW_STEP at
+  // 16 (l % CH), so each instruction covers whole rows; the wide 8-bit loads
+  // take 16 bytes of row l / (RB / 16) + i 1024 / RB at 16 (l % (RB / 16)) (in
+  // load); int4, lane l's run of D / 8 bytes at D / 8 l (1 KB per instruction
+  // at d = 128).
   const uint32_t klane = I4 ? col * RB + (D / 8) * grp : col * RB + 16 * grp;
-  const uint32_t vlane = Gm::crow(l) * RB + VB * (l % Gm::CH);
+  const uint32_t vlane = I4 ? VB * l : Gm::crow(l) * RB + VB * (l % Gm::CH);
   constexpr int VSTEP = Gm::CROW_STEP * RB;
   auto stages_of = [&](int len) { return (len + TS - 1) / TS; };
 
@@ -366,13 +359,13 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const float c_log2 = a.scale_log2;  // > 0 on this path
   float cl = c_log2;                  // the segment's logit scale (int8: over the rescaled query)
-  uint8_t* vt = vtile + w * Gm::SLOT * SB;
+  uint8_t* vt = I4 ? vtile : vtile + w * Gm::SLOT * SB;  // int4: no V tile
 
   // One stage in registers: K rows in MFMA operand layout (lane -> token row
-  // col, 16 bytes at d = 32 ks + 8 grp), V rows as loaded (16-bit: bytes
-  // 16 l + 1024 i of the stage; 8- and 4-bit: lane -> row l / 4, a quarter row
-  // at byte RB / 4 (l % 4)), and the query fragments when the stage starts a
-  // segment.
+  // col, 16 bytes at d = 32 ks + 8 grp), V as loaded (16-bit: bytes
+  // 16 l + 1024 i of the stage; 8-bit: 16 bytes of a row per load; int4: the
+  // lane's run of operand-order bytes per block), and the query rows when the
+  // stage starts a segment.
   struct Stage {
     u32x4 k[SB][NKL];  // block j of the stage: tokens 16 j .. 16 j + 15
     VT v[SB][NV];
@@ -429,8 +422,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       // infinity, and 0 times those is not 0 (K rows past the length are harmless:
       // their scores are replaced by -inf).  Paged: a block has all 16 rows; the
       // wide 8-bit V loads clamp their row likewise (measured faster here than
-      // zeroing), the others read every row and zero those past the length
-      // after the load (compute).
+      // zeroing), the 16-bit ones read every row and zero those past the length
+      // after the load (compute); every int4 code is a finite value, so its V
+      // needs neither (weight 0 times a finite value is 0).
       const uint8_t* kb = kp + row0 * RB;
       const uint8_t* vb = vp + row0 * RB;
       if constexpr (PAGED) {
@@ -591,24 +585,10 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         f32x4 o = oacc[db] * (FP8 ? inv * sa.v_scale : inv);
-        if constexpr (I8) o -= has_w ? kI8Offset : 0.f;  // V carried the codes + 1152
-        if constexpr (I4) {
-          // rows 16 db + 4 grp + i hold slots (4 grp + i) % 8 of their group of 8,
-          // i.e. channels c0 + {0, 4, 1, 5} with c0 = 16 db + 8 (grp / 2) + 2 (grp % 2);
-          // i = 0, 1 are slots of the form 1024 + u, i = 2, 3 of the form 1024 + 16 u
-          if (has_w) {
-            o[0] -= kI4RawOff, o[1] -= kI4RawOff;
-            o[2] = (o[2] - kI4RawOff16) * 0.0625f, o[3] = (o[3] - kI4RawOff16) * 0.0625f;
-          }
-          const int c0 = 16 * db + 8 * (grp >> 1) + 2 * (grp & 1);
-          const float2 s01 = *reinterpret_cast<const float2*>(sa.v_scales + (size_t)g * D + c0);
-          const float2 s45 = *reinterpret_cast<const float2*>(sa.v_scales + (size_t)g * D + c0 + 4);
-          *reinterpret_cast<float2*>(a.part_o + pidx * D + c0) = float2{o[0] * s01.x, o[2] * s01.y};
-          *reinterpret_cast<float2*>(a.part_o + pidx * D + c0 + 4) = float2{o[1] * s45.x, o[3] * s45.y};
-        } else {
-          if constexpr (QS) o *= *reinterpret_cast<const f32x4*>(sa.v_scales + (size_t)g * D + 16 * db + 4 * grp);
-          *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = o;
-        }
+        if constexpr (I8) o -= has_w ? kI8Offset : 0.f;   // V carried the codes + 1152
+        if constexpr (I4) o -= has_w ? kI4VOffset : 0.f;  // V carried the codes + 1032
+        if constexpr (QS) o *= *reinterpret_cast<const f32x4*>(sa.v_scales + (size_t)g * D + 16 * db + 4 * grp);
+        *reinterpret_cast<f32x4*>(a.part_o + pidx * D + 16 * db + 4 * grp) = o;
       }
       if (grp == 0) a.part_lse[pidx] = e_tot > 0.f ? (m + __log2f(e_tot)) * kLn2 : kNegInf;
     }
@@ -646,7 +626,7 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     for (int j = 0; j < SB; ++j)
 #pragma unroll
       for (int i = 0; i < NV; ++i) vraw[j][i] = S.v[j][i];
-    if constexpr (PAGED && !WV) {
+    if constexpr (PAGED && !WV && !I4) {
       if (t0 + TS > c.len) {
 #pragma unroll
         for (int j = 0; j < SB; ++j)
@@ -670,14 +650,12 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
           *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = lo;
           *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch + 1)) = hi;
         }
-      } else {
+      } else if constexpr (!I4) {
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
           const VT raw = vraw[j][i];
           u32x4 x;
-          if constexpr (I4) {
-            x = i4x8_to_f16_biased(raw);  // V: biased values, slot order
-          } else if constexpr (I8) {
+          if constexpr (I8) {
             x = i8x8_to_f16_biased(raw);      // V: the codes + 1152
           } else if constexpr (FP8) {
             x = fp8x8_to<T>(raw);
@@ -787,7 +765,20 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4*)(vt + (16 * j + vrow) * ROWB + 16 * ch + 2 * ((4 * vq) & 7)));
     };
-    if constexpr (SB % 2 == 0) {
+    if constexpr (I4) {
+      // operands straight from the loaded runs: lane (i, g) holds channel
+      // 16 db + i, tokens 4 g .. 4 g + 3 of blocks j and j + 1, as the
+      // transposing reads give the other caches
+#pragma unroll
+      for (int j = 0; j < SB; j += 2) {
+        const u32x4 pp = u32x4{pf[j][0], pf[j][1], pf[j + 1][0], pf[j + 1][1]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 v0 = i4_v_operand(vraw[j][0][db >> 1], db), v1 = i4_v_operand(vraw[j + 1][0][db >> 1], db);
+          oacc[db] = mfma16k32<TC>(u32x4{v0[0], v0[1], v1[0], v1[1]}, pp, oacc[db]);
+        }
+      }
+    } else if constexpr (SB % 2 == 0) {
 #pragma unroll
       for (int j = 0; j < SB; j += 2) {
         const u32x4 pp = u32x4{pf[j][0], pf[j][1], pf[j + 1][0], pf[j + 1][1]};

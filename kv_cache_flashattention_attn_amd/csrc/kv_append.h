@@ -191,12 +191,19 @@ __global__ void __launch_bounds__(256) kv_append_8bit_kernel(Append8Args a) {
 }
 
 // int4 cache: the int8 rule with codes clamped to [-7, 7], two per byte
-// (element 2i in the low nibble, 2i + 1 in the high one, 4-bit two's
-// complement).  One thread quantizes 16 consecutive elements of a K row and of
-// the V row into 8 bytes each.
+// (4-bit two's complement).  K rows: element 2i in the low nibble, 2i + 1 in
+// the high one.  V: each (block, KV head) of 16 tokens x d channels is 8 d
+// bytes in the order the decode's P V product reads them: 64 runs of d / 8
+// bytes, run 16 g + i holding tokens 4 g .. 4 g + 3 of channels i + 16 m;
+// byte 4 w + j of a run holds token 4 g + kI4VTok[j] of channel 32 w + i (low
+// nibble) and 32 w + 16 + i (high nibble).  So a byte holds one token, and an
+// append writes whole bytes.  One thread quantizes 32 consecutive channels of
+// a token: 16 bytes of its K row, and 16 single bytes of V (channels
+// 32 c + i and 32 c + 16 + i, i = 0 .. 15).
+__device__ __forceinline__ constexpr int kI4VTok(int j) { return j == 1 ? 2 : j == 2 ? 1 : j; }  // self-inverse
 template <typename TIN>
 __global__ void __launch_bounds__(256) kv_append_int4_kernel(Append8Args a) {
-  const int per_row = a.d / 16;
+  const int per_row = a.d / 32;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.B * a.H_kv * a.n_new * per_row;
   if (idx >= total) return;
@@ -221,18 +228,23 @@ __global__ void __launch_bounds__(256) kv_append_int4_kernel(Append8Args a) {
     if (c == 0) raise_device_error(2);
     return;
   }
-  const int64_t dst = (((int64_t)blk * a.H_kv + h) * 16 + (p & 15)) * (a.d / 2) + 8 * c;
-  const int64_t src = row * a.d + 16 * c;
-  const float* ksc = a.k_scales + (int64_t)h * a.d + 16 * c;
-  const float* vsc = a.v_scales + (int64_t)h * a.d + 16 * c;
-  uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+  const int r = (int)(p & 15);                                   // token of the block
+  const int64_t base = ((int64_t)blk * a.H_kv + h) * 8 * a.d;   // the (block, KV head)'s bytes
+  const int64_t src = row * a.d + 32 * c;
+  const float* ksc = a.k_scales + (int64_t)h * a.d + 32 * c;
+  const float* vsc = a.v_scales + (int64_t)h * a.d + 32 * c;
+  uint32_t kw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < 32; ++e)
     kw[e >> 3] |= (f32_to_i8(in_to_f32<TIN>(a.k_new, src + e), ksc[e], 7.f) & 0xFu) << (4 * (e & 7));
-    vw[e >> 3] |= (f32_to_i8(in_to_f32<TIN>(a.v_new, src + e), vsc[e], 7.f) & 0xFu) << (4 * (e & 7));
+  *reinterpret_cast<uint4*>(a.k_pool + base + (int64_t)r * (a.d / 2) + 16 * c) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+  const int64_t vrun0 = base + (int64_t)(16 * (r >> 2)) * (a.d / 8) + 4 * c + kI4VTok(r & 3);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t lo = f32_to_i8(in_to_f32<TIN>(a.v_new, src + i), vsc[i], 7.f) & 0xFu;
+    const uint32_t hi = f32_to_i8(in_to_f32<TIN>(a.v_new, src + 16 + i), vsc[16 + i], 7.f) & 0xFu;
+    a.v_pool[vrun0 + (int64_t)i * (a.d / 8)] = (uint8_t)(lo | (hi << 4));
   }
-  *reinterpret_cast<uint2*>(a.k_pool + dst) = make_uint2(kw[0], kw[1]);
-  *reinterpret_cast<uint2*>(a.v_pool + dst) = make_uint2(vw[0], vw[1]);
 }
 
 // kv_copy_blocks: duplicate whole physical blocks (every KV head) of the K and V

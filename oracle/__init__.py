@@ -36,7 +36,7 @@ from .decode import cached_decode, naive_decode, decode_step, chunk_step
 from .fp8 import E4M3_VALUES, e4m3_round, e4m3_value, quantize, decode_step_fp8, prefill_fp8
 from .block_pool import FreeListPool, NoBlocks, blocks_for, simulate
 from .int8 import (quantize_int8, dequantize_int8, decode_step_int8, quantize_int4, pack_int4, unpack_int4,
-                   decode_step_int4)
+                   decode_step_int4, int4_v_position, int4_v_to_pool, int4_v_from_pool)
 
 __all__ = [
     "decode_bits", "kv_bytes", "kv_head_of",
@@ -47,5 +47,5 @@ __all__ = [
     "E4M3_VALUES", "e4m3_round", "e4m3_value", "quantize", "decode_step_fp8", "prefill_fp8",
     "FreeListPool", "NoBlocks", "blocks_for", "simulate",
     "quantize_int8", "dequantize_int8", "decode_step_int8", "quantize_int4", "pack_int4", "unpack_int4",
-    "decode_step_int4",
+    "decode_step_int4", "int4_v_position", "int4_v_to_pool", "int4_v_from_pool",
 ]

@@ -19,8 +19,15 @@ group of channels sharing a scale is the special case of equal entries.
     value = code * s
 
 int4 (the same page and section): the same scales and rounding with codes
-clamped to [-7, 7], stored two per byte, element 2i in the low nibble and
-element 2i + 1 in the high nibble, each as 4-bit two's complement.
+clamped to [-7, 7], two per byte as 4-bit two's complement.  K rows: element
+2i in the low nibble and element 2i + 1 in the high nibble.  V: each (block,
+KV head) of 16 tokens x d channels is 8 d bytes in the order the decode's
+P V product reads them (``int4_v_position``): 64 runs of d / 8 bytes, run
+16 g + i holding tokens 4 g .. 4 g + 3 of channels i, i + 16, i + 32, ...;
+byte 4 w + j of a run holds token 4 g + (0, 2, 1, 3)[j] of channel
+32 w + i (low nibble) and 32 w + 16 + i (high nibble).  The pool keeps the
+shape [num_blocks, H_kv, 16, d / 2]; only the order of a block's bytes
+differs from K's rows.
 
 Pins (tests/test_oracle_int8.py): hand values, brute-force nearest-integer
 rounding, ties, saturation, the per-channel scale selecting the right channel
@@ -111,15 +118,57 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return np.where(out >= 8, out - 16, out).astype(np.int8)
 
 
+_V_BYTE_OF_TOKEN = (0, 2, 1, 3)  # byte j of a 4-byte word holds token (0, 2, 1, 3)[j] of its group
+
+
+def int4_v_position(t: int, c: int, d: int):
+    """(byte offset, nibble) of token t (0..15), channel c (0..d-1) within one
+    (block, KV head) of the int4 V pool (8 d bytes; nibble 0 low, 1 high).  The
+    layout pairs channel groups c // 16, so d is a multiple of 32."""
+    if d % 32 or not (0 <= t < 16 and 0 <= c < d):
+        raise ValueError("int4 V pool: d must be a multiple of 32, 0 <= t < 16, 0 <= c < d")
+    g, i, m = t // 4, c % 16, c // 16
+    run = 16 * g + i
+    return run * (d // 8) + 4 * (m // 2) + _V_BYTE_OF_TOKEN.index(t % 4), m % 2
+
+
+def int4_v_to_pool(rows: np.ndarray) -> np.ndarray:
+    """V bytes [..., 16, d / 2] in row order (``pack_int4`` of each token) ->
+    the same codes in the pool's order, same shape."""
+    codes = unpack_int4(rows).astype(np.int16) & 0xF  # [..., 16, d]
+    d = codes.shape[-1]
+    out = np.zeros(rows.shape[:-2] + (8 * d,), np.int16)
+    for t in range(16):
+        for c in range(d):
+            off, hi = int4_v_position(t, c, d)
+            out[..., off] |= codes[..., t, c] << (4 * hi)
+    return out.astype(np.uint8).reshape(rows.shape)
+
+
+def int4_v_from_pool(blocks: np.ndarray) -> np.ndarray:
+    """Inverse of ``int4_v_to_pool``: V bytes in the pool's order -> row order."""
+    d = 2 * blocks.shape[-1]
+    flat = blocks.reshape(blocks.shape[:-2] + (8 * d,)).astype(np.int16)
+    codes = np.zeros(blocks.shape[:-2] + (16, d), np.int16)
+    for t in range(16):
+        for c in range(d):
+            off, hi = int4_v_position(t, c, d)
+            codes[..., t, c] = (flat[..., off] >> (4 * hi)) & 0xF
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
 def decode_step_int4(cache: PagedCache, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
                      lens: np.ndarray, scale: float, dtype: str, k_scales: np.ndarray, v_scales: np.ndarray,
                      heads=None):
     """``decode_step_int8`` over int4 pools: ``cache`` holds packed bytes
-    [num_blocks, H_kv, 16, d / 2] and is modified in place."""
+    [num_blocks, H_kv, 16, d / 2] (V in the pool's order) and is modified in place."""
     B = k_new.shape[0]
     kq = np.stack([pack_int4(quantize_int4(k_new[b], dtype, k_scales)) for b in range(B)])
     vq = np.stack([pack_int4(quantize_int4(v_new[b], dtype, v_scales)) for b in range(B)])
-    cache.append(kq, vq, lens)
+    rows = PagedCache(cache.k, int4_v_from_pool(cache.v), cache.table)
+    rows.append(kq, vq, lens)
+    cache.k[...] = rows.k
+    cache.v[...] = int4_v_to_pool(rows.v)
     _, H_q, d = q.shape
     n_new = k_new.shape[2]
     O = np.full((B, H_q, d), np.nan)
@@ -130,7 +179,7 @@ def decode_step_int4(cache: PagedCache, q: np.ndarray, k_new: np.ndarray, v_new:
         by_b.setdefault(b, []).append(h)
     for b, hs in sorted(by_b.items()):
         n = int(lens[b]) + n_new
-        Kc, Vc = cache.gather(b, n)
+        Kc, Vc = rows.gather(b, n)  # V back in row order
         K = dequantize_int8(unpack_int4(Kc), k_scales)[None]
         V = dequantize_int8(unpack_int4(Vc), v_scales)[None]
         qb = decode_bits(q[b], dtype)[None, :, None, :]

@@ -377,9 +377,12 @@ def int4_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
     ``SFC64(case.seed + 8500)``: ``k_scales``, ``v_scales`` [H_kv, d] float32,
     2^u with u uniform in [-5, -2) and, in every KV head, 4 random key channels
     8x larger; then the pools' packed bytes [num_blocks, H_kv, 16, d / 2], K's
-    then V's: uniform random bytes where a slot holds a token (two uniform codes
+    then V's: uniform random bytes where a byte holds a token (two uniform codes
     in [-8, 7] each; -8 never comes out of quantization but decodes like any
-    code); slots holding none carry 0x00 in K and 0x77 (codes 7, 7) in V.
+    code); bytes of slots holding none carry 0x00 in K and 0x77 (codes 7, 7) in
+    V.  A K byte belongs to the token of its row; V's bytes of a (block, KV
+    head) are in the pool's order, where byte o belongs to token
+    4 ((o // (d / 8)) // 16) + (0, 2, 1, 3)[(o % (d / 8)) % 4].
     """
     out = dict(base) if base is not None else decode_inputs(case, lens=lens)
     lens = out["lens"]
@@ -398,8 +401,11 @@ def int4_decode_inputs(case: DecodeCase, lens: Optional[np.ndarray] = None,
         held[table[b, :nb]] = np.arange(bs)[None, :] < fill[:, None]
     mask = held[:, None, :, None]
     shape = (nblk, Hk, bs, d // 2)
+    o = np.arange(8 * d)
+    vtok = (4 * ((o // (d // 8)) // 16) + np.array([0, 2, 1, 3])[(o % (d // 8)) % 4]).reshape(bs, d // 2)
+    vmask = held[:, None, vtok]
     kp = np.where(mask, rng.integers(0, 256, size=shape, dtype=np.uint8), np.uint8(0x00))
-    vp = np.where(mask, rng.integers(0, 256, size=shape, dtype=np.uint8), np.uint8(0x77))
+    vp = np.where(vmask, rng.integers(0, 256, size=shape, dtype=np.uint8), np.uint8(0x77))
     out.update(k_pool=kp.astype(np.uint8), v_pool=vp.astype(np.uint8), k_scales=ks, v_scales=vs)
     return out
 

@@ -143,14 +143,15 @@ def test_int4_append_image_is_bit_exact(K, dtype, pow2):
     K.kv_append_int4(kp, vp, to_dev(kn, dtype), to_dev(vn, dtype), to_dev_i32(inp["lens"]), table, f32(ks), f32(vs))
     torch.cuda.synchronize()
     assert K.attn_device_error_flags() == 0
-    cache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
+    # the oracle's cache in row order (V's pool order undone), the append, then V back
+    cache = oracle.PagedCache(inp["k_pool"], oracle.int4_v_from_pool(inp["v_pool"]), inp["block_table"])
     kq = np.stack([oracle.pack_int4(oracle.quantize_int4(kn[b], dtype, ks)) for b in range(case.B)])
     vq = np.stack([oracle.pack_int4(oracle.quantize_int4(vn[b], dtype, vs)) for b in range(case.B)])
     cache.append(kq, vq, inp["lens"])
     if pow2:
         assert oracle.quantize_int4(kn[0], dtype, ks)[0, 0, :7].tolist() == [2, 4, -2, 0, 0, 6, 7]
     assert kp.cpu().numpy().tobytes() == cache.k.tobytes(), "K pool image differs"
-    assert vp.cpu().numpy().tobytes() == cache.v.tobytes(), "V pool image differs"
+    assert vp.cpu().numpy().tobytes() == oracle.int4_v_to_pool(cache.v).tobytes(), "V pool image differs"
 
 
 def u8(x):
@@ -180,6 +181,7 @@ def run_int4(K, case, lens=None, heads=None, poison=False, edit=None):
     Oref, Lref = oracle.decode_step_int4(cache, inp["q"], inp["k_new"], inp["v_new"], inp["lens"], case.sm_scale, dt,
                                          inp["k_scales"], inp["v_scales"], heads=heads)
     assert kp.cpu().numpy().tobytes() == cache.k.tobytes(), "K pool image differs"
+    assert vp.cpu().numpy().tobytes() == cache.v.tobytes(), "V pool image differs"
     got_l = lse.cpu().numpy().astype(np.float64)
     if heads is not None:
         idx = tuple(np.array(heads).T)

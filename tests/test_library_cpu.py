@@ -110,6 +110,9 @@ def test_append_rejects_bad_arguments():
     assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 0, 128, 64, 16, 0, 0, 2, None) == 1
     # contiguous with max_len 0
     assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 1, 128, 0, 16, 0, 0, 2, None) == 1
+    # int4: V pairs channel groups, so d must be a multiple of 32 (16 is refused, 32 gets past the check)
+    assert L.kv_append_int4(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 16, 4, 4, 2, FAKE, FAKE, None) == 2
+    assert L.kv_append_int4(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 32, 16, 0, 4, 2, FAKE, FAKE, None) == 1
 
 
 @pytest.mark.parametrize("args,code", [

@@ -2,6 +2,7 @@
 by brute force, ties, saturation, channel/head selection, decode over the
 dequantized cache."""
 import numpy as np
+import pytest
 
 import oracle
 import synth
@@ -86,6 +87,45 @@ def test_int4_packing_by_hand():
     assert np.array_equal(oracle.pack_int4(oracle.unpack_int4(every)), every)
 
 
+def test_int4_v_pool_order_by_hand():
+    # positions worked out from the layout: run 16 (t // 4) + c % 16 of d / 8 bytes,
+    # byte 4 ((c // 16) // 2) + (0, 2, 1, 3).index(t % 4), nibble (c // 16) % 2
+    assert oracle.int4_v_position(0, 0, 128) == (0, 0)
+    assert oracle.int4_v_position(5, 37, 128) == (21 * 16 + 4 + 2, 0)
+    assert oracle.int4_v_position(14, 127, 128) == (63 * 16 + 12 + 1, 1)
+    assert oracle.int4_v_position(3, 16, 128) == (3, 1)
+    assert oracle.int4_v_position(9, 50, 64) == (34 * 8 + 4 + 2, 1)
+    # one code placed through the row packing lands there, and nowhere else
+    for t, c, d in ((5, 37, 128), (14, 127, 128), (9, 50, 64)):
+        codes = np.zeros((16, d), np.int8)
+        codes[t, c] = -3
+        pool = oracle.int4_v_to_pool(oracle.pack_int4(codes)).ravel()
+        off, hi = oracle.int4_v_position(t, c, d)
+        want = np.zeros(8 * d, np.uint8)
+        want[off] = 0xD << (4 * hi)  # -3 as a 4-bit two's complement nibble
+        assert np.array_equal(pool, want)
+
+
+def test_int4_v_pool_order_is_one_token_per_byte_and_a_permutation():
+    for d in (64, 128):
+        seen = {}
+        for t in range(16):
+            for c in range(d):
+                off, hi = oracle.int4_v_position(t, c, d)
+                assert 0 <= off < 8 * d and (off, hi) not in seen
+                seen[(off, hi)] = (t, c)
+        assert len(seen) == 16 * d
+    with pytest.raises(ValueError):
+        oracle.int4_v_position(0, 0, 16)
+        for off in range(8 * d):  # a byte holds one token, channels c and c + 16
+            (t0, c0), (t1, c1) = seen[(off, 0)], seen[(off, 1)]
+            assert t0 == t1 and c1 == c0 + 16
+    rng = np.random.default_rng(3)
+    x = rng.integers(0, 256, size=(3, 2, 16, 32), dtype=np.uint8)
+    assert np.array_equal(oracle.int4_v_to_pool(oracle.int4_v_from_pool(x)), x)
+    assert np.array_equal(oracle.int4_v_from_pool(oracle.int4_v_to_pool(x)), x)
+
+
 def test_int4_quantize_clamps_to_seven():
     x = np.array([6.4, 6.5, 7.5, 100.0, -7.5, -100.0, 2.5, np.nan], np.float32).reshape(1, 1, 8)
     s = np.ones((1, 8), np.float32)
@@ -93,15 +133,16 @@ def test_int4_quantize_clamps_to_seven():
 
 
 def test_int4_decode_step_is_attention_over_dequantized_values():
-    case = synth.DecodeCase("i4", 3, 8, 2, 16, "bf16", 1, 40, True, seed=35)
+    case = synth.DecodeCase("i4", 3, 8, 2, 32, "bf16", 1, 40, True, seed=35)
     inp = synth.int4_decode_inputs(case)
-    assert inp["k_pool"].shape[-1] == 8
+    assert inp["k_pool"].shape[-1] == 16
     cache = oracle.PagedCache(inp["k_pool"], inp["v_pool"], inp["block_table"])
     O, L = oracle.decode_step_int4(cache, inp["q"], inp["k_new"], inp["v_new"], inp["lens"], case.sm_scale, "bf16",
                                    inp["k_scales"], inp["v_scales"])
+    rows = oracle.PagedCache(cache.k, oracle.int4_v_from_pool(cache.v), inp["block_table"])
     for b in range(case.B):
         n = int(inp["lens"][b]) + 1
-        Kc, Vc = cache.gather(b, n)
+        Kc, Vc = rows.gather(b, n)
         # nibbles decoded one by one, apart from unpack_int4
         def val(byte_arr, scales):
             out = np.empty(byte_arr.shape[:-1] + (2 * byte_arr.shape[-1],))
