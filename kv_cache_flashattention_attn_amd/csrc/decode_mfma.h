@@ -650,20 +650,13 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
           *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = lo;
           *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch + 1)) = hi;
         }
-      } else if constexpr (!I4) {
+      } else if constexpr (!Q8) {
+        // 16-bit V: the loaded chunks as they are (int4 V needs no tile: its
+        // operands are built from the loaded runs in the P V step below)
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
-          const VT raw = vraw[j][i];
-          u32x4 x;
-          if constexpr (I8) {
-            x = i8x8_to_f16_biased(raw);      // V: the codes + 1152
-          } else if constexpr (FP8) {
-            x = fp8x8_to<T>(raw);
-          } else {
-            x = raw;
-          }
           const int r = 16 * j + Gm::crow(l) + i * Gm::CROW_STEP, ch = l % Gm::CH;
-          *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = x;
+          *reinterpret_cast<u32x4*>(vt + r * ROWB + 16 * vchunk(r, ch)) = vraw[j][i];
         }
       }
       sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
