@@ -48,7 +48,8 @@ namespace attn {
 
 constexpr int kDecStage = 16;     // tokens per stage (one cache block)
 constexpr int kDecWaves = 4;      // waves per workgroup
-constexpr int kDecMinShare = 16;  // stages per wave at least (bounds the pieces per segment)
+constexpr int kDecMinShare = 16;  // 16-token blocks per wave at least: a share covers 256 tokens or more,
+                                  // which bounds the pieces per segment
 
 // Pieces a segment of at most `capacity` tokens can be cut into.
 inline constexpr int dec_max_pieces(int capacity) {
@@ -299,7 +300,9 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
     total += wave_sum(n);
   }
   total = __builtin_amdgcn_readfirstlane(total);
-  const int share = max(kDecMinShare, (total + n_workers - 1) / n_workers);
+  // at least 256 tokens per share whatever the stage size (SB blocks per stage),
+  // so a stage of several blocks does not leave waves idle on small problems
+  const int share = max(kDecMinShare / SB, (total + n_workers - 1) / n_workers);
   const int beg = worker * share;
   if (beg >= total) return;
   const int end = min(total, beg + share);
