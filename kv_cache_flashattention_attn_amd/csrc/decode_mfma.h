@@ -10,10 +10,9 @@
 // Work split (persistent, balanced by bytes): the cache is cut into stages of
 // one segment = (sequence, KV head [x group of 16 query heads]); a stage is
 // one block of 16 tokens of a paged cache ("KV Cache:推理慢的真正原因",
-// 工程优化手段 / 1. PagedAttention), or two blocks of an int8 cache and four of
-// an int4 cache, so that a stage holds as many bytes.  The stages of all
-// segments, laid end to
-// end, form one stream; the grid is a fixed number of waves (as many as fit
+// 工程优化手段 / 1. PagedAttention), or several blocks of an int8 or int4
+// cache (SB below).  The stages of all segments, laid end to end, form one
+// stream; the grid is a fixed number of waves (as many as fit
 // on the GPU at once) and wave k takes an equal contiguous share of the
 // stream.  A wave never waits for another:
 //  * each stage's K rows are loaded straight into MFMA operand registers and
@@ -34,7 +33,8 @@
 //    stage exceeds it by 2^8, so the O accumulator is rarely rescaled;
 //  * O^T += V^T P^T with v_mfma_f32_16x16x16 (16x16x32 over two blocks when a
 //    stage has several): P^T comes straight from the S^T registers (rounded
-//    to 16 bits), V^T from ds_read_b64_tr_b16 on the row-major V stage.
+//    to 16 bits), V^T from ds_read_b64_tr_b16 on the row-major V stage (int4:
+//    widened from the loaded runs).
 // Where a wave's share starts or ends inside a segment, or a segment ends, the
 // wave writes that piece's normalised partial output and lse (piece p of a
 // segment belongs to the p-th wave whose share overlaps it);
@@ -226,12 +226,14 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
       return c ^ Gm::swz_v(r);
   };
   // Cache blocks per stage.  A 16-bit stage of one block is 128 bytes per lane
-  // at d = 128; the int8 and int4 stages take as many blocks as give the same
-  // bytes, so the per-stage work (the softmax's reductions, the loop, the
-  // bookkeeping) is spread over as many bytes and as many bytes are in flight.
+  // at d = 128; the int8 stage takes as many blocks as give the same bytes (two
+  // at d = 128, four at d = 64), so the per-stage work (the softmax's
+  // reductions, the loop, the bookkeeping) is spread over as many bytes and as
+  // many bytes are in flight.  The int4 stage is four blocks at either d (at
+  // d = 64, four measured 6% faster than the eight that give the same bytes).
   // The FP8 stage keeps one block: two measured about 1% slower there, against
   // about 2.5% faster for int8.
-  constexpr int SB = QS ? 256 / RB : 1;
+  constexpr int SB = I4 ? 4 : I8 ? 256 / RB : 1;
   constexpr int TS = kDecStage * SB;  // tokens per stage
   // vector memory instructions every stage's load issues (K, then V), before
   // any query row or key-scale copy
