@@ -231,9 +231,10 @@ decode_mfma_kernel(DecodeStreamArgs sa, const int32_t* __restrict__ lens, const 
   // reductions, the loop, the bookkeeping) is spread over as many bytes and as
   // many bytes are in flight.  The int4 stage is four blocks at either d (at
   // d = 64, four measured 6% faster than the eight that give the same bytes).
-  // The FP8 stage keeps one block: two measured about 1% slower there, against
-  // about 2.5% faster for int8.
-  constexpr int SB = I4 ? 4 : I8 ? 256 / RB : 1;
+  // The 16-bit and FP8 stages keep one block at d = 128 (two measured about 1%
+  // slower for FP8, against about 2.5% faster for int8) and take two at d = 64,
+  // where a block is half the bytes (1-2% faster there).
+  constexpr int SB = I4 ? 4 : I8 ? 256 / RB : (D == 64 ? 2 : 1);
   constexpr int TS = kDecStage * SB;  // tokens per stage
   // vector memory instructions every stage's load issues (K, then V), before
   // any query row or key-scale copy
