@@ -31,8 +31,9 @@ differs from K's rows.
 
 Pins (tests/test_oracle_int8.py): hand values, brute-force nearest-integer
 rounding, ties, saturation, the per-channel scale selecting the right channel
-and head, nibble packing, and decode steps equal to attention over the
-dequantized cache.
+and head, nibble packing, the int4 V pool's order (positions worked out by
+hand, one token per byte, round trips over random bytes), and decode steps
+equal to attention over the dequantized cache.
 """
 from __future__ import annotations
 
