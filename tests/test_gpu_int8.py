@@ -128,8 +128,11 @@ SPECIAL4 = np.array([2.5, 3.5, -2.5, -0.5, 0.5, 6.5, 7.5, 30.0, -30.0, 0.0, -0.0
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("pow2", [True, False])
-def test_int4_append_image_is_bit_exact(K, dtype, pow2):
-    case = synth.DecodeCase("i4", 5, 4, 2, 128, dtype, 0, 60, True, 240 + len(dtype), n_new=19)
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_int4_append_image_is_bit_exact(K, dtype, pow2, d):
+    """Both pools byte for byte after a 19-token append, V in the pool's operand
+    order (runs of d / 8 bytes) at every head dimension the append takes."""
+    case = synth.DecodeCase("i4", 5, 4, 2, d, dtype, 0, 60, True, 240 + len(dtype) + d, n_new=19)
     inp = synth.int4_decode_inputs(case)
     ks, vs = inp["k_scales"].copy(), inp["v_scales"].copy()
     if pow2:
